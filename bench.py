@@ -1,0 +1,282 @@
+"""Benchmark of the block-sparse attention layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one layer: block pooling, scoring + selection, and attention over
+all heads of the workload, with inputs already resident in HBM.  Default
+workload: dit_image_8k (bf16, B=1, 24 heads, N=8192, d=128, block 64, top-k
+at density 0.15, 0th-order tail).  Prints one JSON line.
+
+Stage times come from HIP events recorded on the stream the library launches
+on (torch's current stream) around every stage of every timed step.  The
+effective throughput counts algorithmic work only: 4*d flops per allowed
+exact (query, key) pair and per (query, tail block) pair, from the selection
+the run produced.  The CPU baseline times the oracle on a bounded sample of
+the same workload (whole heads; heads are independent).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_F32_MFMA_TFLOPS = 157.3   # MI355X fp32 matrix peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "block-sparse attn fwd ms/layer + effective TFLOP/s (MFMA %) at N=8K–256K"
+KERNEL_SOURCES = ["pool.hip", "select.hip", "attn_bf16.hip", "attn_f32.hip", "device_common.h"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="dit_image_8k")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=12.0,
+                   help="CPU seconds the oracle sample may take (whole heads)")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="also run one device copy of this size (counter calibration runs)")
+    p.add_argument("--dense", action="store_true",
+                   help="attend every eligible block (caller lists), the dense comparison run")
+    return p.parse_args()
+
+
+def work_units(idx, cnt, N, block, causal, approx):
+    """Allowed exact (i, j) pairs and (i, tail block) pairs of a selection."""
+    B, Hq, M = cnt.shape
+    n = np.array([min(block, N - J * block) for J in range(M)], dtype=np.int64)
+    exact = 0
+    tail = 0
+    for b in range(B):
+        for h in range(Hq):
+            for I in range(M):
+                c = int(cnt[b, h, I])
+                sel = idx[b, h, I, :c]
+                nI = int(n[I])
+                off = sel[sel != I] if causal else sel
+                exact += nI * int(n[off].sum())
+                if causal and (sel == I).any():
+                    exact += nI * (nI + 1) // 2
+                if approx:
+                    n_elig = I + 1 if causal else M
+                    tail += nI * (n_elig - c)
+    return exact, tail
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_attention_08_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_attn_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_sources_sha") != kernel_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, seed, budget_s):
+    """Time the oracle (as it stands) on whole KV groups of the workload until
+    the budget is used; returns effective TFLOP/s with the same work count."""
+    import oracle
+    from synth import make_group
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    G = wl.Hq // wl.Hkv
+    spent = 0.0
+    flops = 0.0
+    heads = 0
+    g = 0
+    while g < wl.Hkv and (spent < budget_s or heads == 0):
+        q, k, v = make_group(wl, seed, 0, g)
+        t0 = time.perf_counter()
+        r = oracle.forward(q[None], k[None, None], v[None, None], block=wl.block,
+                           causal=wl.causal, approx=wl.approx, mode=wl.select, alpha=wl.alpha,
+                           density=wl.density)
+        spent += time.perf_counter() - t0
+        idx, cnt = oracle.mask_to_lists(r["mask"])
+        ex, tl = work_units(idx, cnt, wl.N, wl.block, wl.causal, wl.approx)
+        flops += 4.0 * wl.d * (ex + tl)
+        heads += G
+        g += 1
+    return {
+        "value": flops / spent / 1e12, "unit": "TFLOP/s (effective)", "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{heads} of {wl.Hq} query heads (KV groups 0..{g - 1}), full sequence, "
+                  f"float64 numpy oracle: pool+score+select+attend, {spent:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_sparse_attention_08_amd as bsa
+    from synth import get_config, make_inputs
+
+    wl = get_config(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q, k, v = make_inputs(wl, args.seed)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    qd = torch.from_numpy(q).to(tdt).to(dev)
+    kd = torch.from_numpy(k).to(tdt).to(dev)
+    vd = torch.from_numpy(v).to(tdt).to(dev)
+    del q, k, v
+    desc = bsa.make_desc(wl.B, wl.Hq, wl.Hkv, wl.N, wl.d, block=wl.block, dtype=wl.dtype,
+                         alpha=wl.alpha if wl.select == "alpha" else None,
+                         density=wl.density if wl.select == "density" else None,
+                         causal=wl.causal, approx=wl.approx)
+    ws = bsa.Workspace(desc, device=dev)
+    out = torch.empty_like(qd)
+    M = wl.M
+    dense_idx = dense_cnt = None
+    if args.dense:
+        idx = np.zeros((wl.B, wl.Hq, M, M), np.int32)
+        idx[...] = np.arange(M, dtype=np.int32)
+        cnt = np.full((wl.B, wl.Hq, M), M, np.int32)
+        if wl.causal:
+            cnt[...] = np.arange(1, M + 1, dtype=np.int32)
+        dense_idx, dense_cnt = torch.from_numpy(idx).to(dev), torch.from_numpy(cnt).to(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        bsa.block_pool(desc, qd, kd, vd, ws.q_bar, ws.k_bar, ws.v_sum)
+        if ev:
+            ev[1].record()
+        bsa.select(desc, ws.q_bar, ws.k_bar, ws.blk_idx, ws.blk_cnt)
+        if ev:
+            ev[2].record()
+        if args.dense:
+            bsa.fwd(desc, qd, kd, vd, ws.k_bar, ws.v_sum, dense_idx, dense_cnt, out)
+        else:
+            bsa.fwd(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.blk_idx, ws.blk_cnt, out)
+        if ev:
+            ev[3].record()
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b_ = torch.empty_like(a)
+        b_.copy_(a)
+        torch.cuda.synchronize()
+        del a, b_
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: warmup {args.warmup} done", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_pool = np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    ms_sel = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    ms_fwd = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+    ms_step = wall * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # algorithmic work of this selection
+    if args.dense:
+        idx_h, cnt_h = dense_idx.cpu().numpy(), dense_cnt.cpu().numpy()
+    else:
+        idx_h, cnt_h = ws.blk_idx.cpu().numpy(), ws.blk_cnt.cpu().numpy()
+    ex, tl = work_units(idx_h, cnt_h, wl.N, wl.block, wl.causal, wl.approx and not args.dense)
+    flops = 4.0 * wl.d * (ex + tl)
+    elt = 2 if wl.dtype == "bf16" else 4
+    n_pool_heads = wl.Hq + wl.Hkv * (2 if wl.approx else 1)
+    pool_bytes = wl.B * n_pool_heads * (wl.N * wl.d * elt + M * wl.d * 4)
+    n_elig = wl.B * wl.Hq * (M * (M + 1) // 2 if wl.causal else M * M)
+    sel_flops = 2.0 * wl.d * n_elig
+    sel_bytes = wl.B * (wl.Hq + wl.Hkv) * M * wl.d * 4 + 4 * (int(cnt_h.sum()) + cnt_h.size)
+    eff_tflops_fwd = flops / (ms_fwd * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    traffic = read_traffic(wl.name) if not args.dense else None
+    eligible_blocks = n_elig
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name + ("+dense" if args.dense else ""), "B": wl.B,
+                   "heads_q": wl.Hq, "heads_kv": wl.Hkv, "seq_len": wl.N, "head_dim": wl.d,
+                   "block": wl.block, "causal": wl.causal,
+                   "selection": (f"alpha={wl.alpha}" if wl.select == "alpha"
+                                 else f"density={wl.density}") if not args.dense else "all",
+                   "tail": bool(wl.approx and not args.dense), "parallelism": "single-gpu"},
+        "roofline": {
+            "bound": "mfma", "kernel": "attn_bf16_kernel" if wl.dtype == "bf16" else "attn_f32_kernel",
+            "achieved": round(eff_tflops_fwd, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(eff_tflops_fwd / peak, 4),
+            "traffic": traffic,
+        },
+        "stages": {
+            "pool_ms": round(ms_pool, 4), "select_ms": round(ms_sel, 4), "fwd_ms": round(ms_fwd, 4),
+            "pool_GBps": round(pool_bytes / (ms_pool * 1e-3) / 1e9, 1),
+            "pool_hbm_frac": round(pool_bytes / (ms_pool * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "select_TFLOPs": round(sel_flops / (ms_sel * 1e-3) / 1e12, 2),
+            "pool_select_hbm_frac": round((pool_bytes + sel_bytes) / ((ms_pool + ms_sel) * 1e-3)
+                                          / 1e9 / PEAK_HBM_GBS, 4),
+            "exact_pairs": int(ex), "tail_pairs": int(tl), "algorithmic_gflop": round(flops / 1e9, 3),
+            "selected_blocks": int(cnt_h.sum()), "eligible_blocks": int(eligible_blocks),
+            "realised_density": round(float(cnt_h.sum()) / eligible_blocks, 5),
+            "dense_equiv_tflops": round(4.0 * wl.d * wl.B * wl.Hq * wl.N * wl.N
+                                        * (0.5 if wl.causal else 1.0) / (ms_step * 1e-3) / 1e12, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, args.seed, args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+"""Block-sparse attention with pooled block routing for AMD MI355X (gfx950).
+
+Python face of the C ABI in ``include/sparse_attn.h``.  Every step of the
+computation runs in the HIP kernels of ``libsparse_attn.so``; this module only
+checks tensors, marshals pointers and passes torch's current HIP stream.
+torch supplies device memory and streams.
+
+    out = block_sparse_attention(q, k, v, block_size=64, density=0.15)
+    out = block_sparse_attention(q, k, v, block_size=128, alpha=0.5, causal=True,
+                                 approx=False)
+
+q: [B, Hq, N, d], k/v: [B, Hkv, N, d], contiguous, bfloat16 or float32, on
+the GPU.  The three stages are also exposed one by one (``block_pool``,
+``select``, ``fwd``) with caller-owned buffers from ``Workspace``.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+from . import _lib
+from ._lib import SA_DTYPE_BF16, SA_DTYPE_F32, SA_SELECT_ALPHA, SA_SELECT_DENSITY, SaDesc, SparseAttnError
+
+__all__ = [
+    "Workspace", "block_pool", "block_sparse_attention", "buffer_sizes", "fwd", "make_desc",
+    "select", "SparseAttnError", "abi_version",
+]
+
+
+def abi_version() -> int:
+    return int(_lib.lib().sparse_attn_abi_version())
+
+
+def make_desc(B: int, Hq: int, Hkv: int, N: int, d: int, *, block: int, dtype: str,
+              alpha: Optional[float] = None, density: Optional[float] = None,
+              causal: bool = False, approx: bool = True, scale: Optional[float] = None) -> SaDesc:
+    """Descriptor for one problem; exactly one of ``alpha`` / ``density``."""
+    if (alpha is None) == (density is None):
+        raise ValueError("give exactly one of alpha (threshold) or density (top-k)")
+    if dtype not in ("bf16", "f32"):
+        raise ValueError(f"dtype must be 'bf16' or 'f32', not {dtype!r}")
+    return SaDesc(
+        batch=B, heads_q=Hq, heads_kv=Hkv, seq_len=N, head_dim=d, block=block,
+        dtype=SA_DTYPE_BF16 if dtype == "bf16" else SA_DTYPE_F32,
+        select_mode=SA_SELECT_ALPHA if alpha is not None else SA_SELECT_DENSITY,
+        alpha=float(alpha or 0.0), density=float(density or 0.0),
+        scale=float(scale) if scale is not None else 0.0,
+        causal=int(bool(causal)), approx=int(bool(approx)))
+
+
+def buffer_sizes(desc: SaDesc) -> dict:
+    """Bytes of each intermediate buffer (host-only call)."""
+    s = _lib.SaSizes()
+    _lib.check(_lib.lib().sparse_attn_buffer_sizes(desc, s), "sparse_attn_buffer_sizes")
+    return {n: int(getattr(s, n)) for n, _ in s._fields_}
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _m(desc: SaDesc) -> int:
+    return -(-desc.seq_len // desc.block)
+
+
+class Workspace:
+    """Caller-owned intermediates for one descriptor: pooled Q/K (float32),
+    V sums (float32, when the tail is on), block lists and counts (int32)."""
+
+    def __init__(self, desc: SaDesc, device="cuda"):
+        import torch
+        sizes = buffer_sizes(desc)
+        B, Hq, Hkv, d, M = desc.batch, desc.heads_q, desc.heads_kv, desc.head_dim, _m(desc)
+        f32, i32 = torch.float32, torch.int32
+        self.desc = desc
+        self.q_bar = torch.empty((B, Hq, M, d), dtype=f32, device=device)
+        self.k_bar = torch.empty((B, Hkv, M, d), dtype=f32, device=device)
+        self.v_sum = torch.empty((B, Hkv, M, d), dtype=f32, device=device) if desc.approx else None
+        self.blk_idx = torch.empty((B, Hq, M, M), dtype=i32, device=device)
+        self.blk_cnt = torch.empty((B, Hq, M), dtype=i32, device=device)
+        assert self.q_bar.numel() * 4 == sizes["q_bar"] and self.blk_idx.numel() * 4 == sizes["blk_idx"]
+
+
+def block_pool(desc, q, k, v, q_bar, k_bar, v_sum, stream=None) -> None:
+    """Stage 1: block means of q and k, block sums of v (v_sum when approx)."""
+    st = _lib.lib().sparse_attn_block_pool(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(q_bar),
+                                           _ptr(k_bar), _ptr(v_sum), _stream(stream))
+    _lib.check(st, "sparse_attn_block_pool")
+
+
+def select(desc, q_bar, k_bar, blk_idx, blk_cnt, stream=None) -> None:
+    """Stage 2: pooled scores, threshold / top-k selection, ascending block lists."""
+    st = _lib.lib().sparse_attn_select(desc, _ptr(q_bar), _ptr(k_bar), _ptr(blk_idx),
+                                       _ptr(blk_cnt), _stream(stream))
+    _lib.check(st, "sparse_attn_select")
+
+
+def fwd(desc, q, k, v, k_bar, v_sum, blk_idx, blk_cnt, out, stream=None) -> None:
+    """Stage 3: attention over the listed blocks (+ 0th-order tail when approx)."""
+    st = _lib.lib().sparse_attn_fwd(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(k_bar), _ptr(v_sum),
+                                    _ptr(blk_idx), _ptr(blk_cnt), _ptr(out), _stream(stream))
+    _lib.check(st, "sparse_attn_fwd")
+
+
+def _check_tensors(q, k, v):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, d]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must share dtype bfloat16 or float32")
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[2:] != k.shape[2:]:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+
+
+def block_sparse_attention(q, k, v, *, block_size: int = 64, alpha: Optional[float] = None,
+                           density: Optional[float] = None, causal: bool = False,
+                           approx: bool = True, scale: Optional[float] = None,
+                           return_selection: bool = False, workspace: Optional[Workspace] = None,
+                           out=None):
+    """Pool -> select -> attend.  Returns ``out`` (dtype of q), or
+    ``(out, blk_idx, blk_cnt)`` with ``return_selection``."""
+    import torch
+    _check_tensors(q, k, v)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    dt = "bf16" if q.dtype == torch.bfloat16 else "f32"
+    if workspace is None:
+        desc = make_desc(B, Hq, Hkv, N, d, block=block_size, dtype=dt, alpha=alpha, density=density,
+                         causal=causal, approx=approx, scale=scale)
+        buffer_sizes(desc)   # validates before any allocation
+        workspace = Workspace(desc, device=q.device)
+    ws = workspace
+    desc = ws.desc
+    if out is None:
+        out = torch.empty_like(q)
+    block_pool(desc, q, k, v, ws.q_bar, ws.k_bar, ws.v_sum)
+    select(desc, ws.q_bar, ws.k_bar, ws.blk_idx, ws.blk_cnt)
+    fwd(desc, q, k, v, ws.k_bar, ws.v_sum, ws.blk_idx, ws.blk_cnt, out)
+    if return_selection:
+        return out, ws.blk_idx, ws.blk_cnt
+    return out
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

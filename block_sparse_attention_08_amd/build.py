@@ -1,0 +1,91 @@
+"""Build libsparse_attn.so (gfx950) in-tree with hipcc.
+
+    python -m block_sparse_attention_08_amd.build      # or build() from Python
+
+Compiles every ``csrc/*.hip`` to an object under ``_build/`` (in parallel) and
+links them into ``block_sparse_attention_08_amd/lib/libsparse_attn.so``.  The
+library links against the HIP runtime that torch ships, so that a process that
+imports torch first holds a single HIP runtime and torch's streams and device
+pointers are valid inside the library.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIBDIR = os.path.join(PKG, "lib")
+BUILD = os.path.join(ROOT, "_build")
+LIBNAME = "libsparse_attn.so"
+ARCH = "gfx950"
+
+CXXFLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden",
+    "-Wall", "-Wno-unused-function",
+    # keep the compiler from emitting packed fp32 vector ALU instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm toolchain required to build the HIP library)")
+
+
+def _torch_lib_dir() -> str | None:
+    try:
+        import torch  # noqa: F401
+    except Exception:
+        return None
+    d = os.path.join(os.path.dirname(torch.__file__), "lib")
+    return d if os.path.exists(os.path.join(d, "libamdhip64.so")) else None
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("build step failed:\n" + " ".join(cmd) + "\n" + r.stdout + r.stderr)
+    return r.stdout + r.stderr
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile and link; returns the path of the shared library."""
+    hipcc = _hipcc()
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
+
+    def one(pair):
+        src, obj = pair
+        return _run([hipcc, *CXXFLAGS, "-c", src, "-o", obj])
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        for out in ex.map(one, zip(srcs, objs)):
+            if verbose and out.strip():
+                print(out)
+
+    link = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o",
+            os.path.join(LIBDIR, LIBNAME + ".tmp"), *objs]
+    tl = _torch_lib_dir()
+    if tl:
+        # bind to torch's bundled HIP runtime (one runtime per process)
+        link += [f"-L{tl}", f"-Wl,-rpath,{tl}", "-Wl,--disable-new-dtags"]
+    _run(link)
+    os.replace(os.path.join(LIBDIR, LIBNAME + ".tmp"), os.path.join(LIBDIR, LIBNAME))
+    return os.path.join(LIBDIR, LIBNAME)
+
+
+if __name__ == "__main__":
+    path = build(verbose="-v" in sys.argv)
+    print(path)

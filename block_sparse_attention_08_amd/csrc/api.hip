@@ -1,0 +1,138 @@
+// Host side of the C ABI declared in include/sparse_attn.h: argument
+// validation, buffer sizes, and one launch per call on the caller's stream.
+// No allocation, no synchronisation, no state.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/sparse_attn.h"
+#include "launch.h"
+
+#define SA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+sa_status check_desc(const sa_desc* d, sa::Shape* s) {
+  if (!d) return SA_ERR_NULL;
+  if (d->batch < 1 || d->heads_q < 1 || d->heads_kv < 1 || d->seq_len < 1 || d->head_dim < 1 ||
+      d->block < 1)
+    return SA_ERR_SHAPE;
+  if (d->heads_q % d->heads_kv != 0) return SA_ERR_SHAPE;
+  if (d->dtype != SA_DTYPE_F32 && d->dtype != SA_DTYPE_BF16) return SA_ERR_DTYPE;
+  if (d->select_mode != SA_SELECT_ALPHA && d->select_mode != SA_SELECT_DENSITY) return SA_ERR_PARAM;
+  if (d->select_mode == SA_SELECT_ALPHA && !(d->alpha > 0.0 && d->alpha <= 1.0)) return SA_ERR_PARAM;
+  if (d->select_mode == SA_SELECT_DENSITY && !(d->density > 0.0 && d->density <= 1.0))
+    return SA_ERR_PARAM;
+  if ((d->causal != 0 && d->causal != 1) || (d->approx != 0 && d->approx != 1)) return SA_ERR_PARAM;
+  if (isnan(d->scale) || isinf(d->scale)) return SA_ERR_PARAM;
+  if (d->head_dim != 64 && d->head_dim != 128) return SA_ERR_UNSUPPORTED;
+  if (d->block != 64 && d->block != 128) return SA_ERR_UNSUPPORTED;
+  const int M = (d->seq_len + d->block - 1) / d->block;
+  if (M > sa::kMaxBlocks) return SA_ERR_UNSUPPORTED;
+  // every workgroup count and per-row index of the kernels is a 32-bit int
+  const int64_t items = (int64_t)d->batch * (d->heads_q + 2 * (int64_t)d->heads_kv) * M;
+  if (items > INT32_MAX / 2) return SA_ERR_SHAPE;
+  if (s) {
+    s->B = d->batch;
+    s->Hq = d->heads_q;
+    s->Hkv = d->heads_kv;
+    s->N = d->seq_len;
+    s->D = d->head_dim;
+    s->block = d->block;
+    s->M = M;
+    s->dtype = d->dtype;
+  }
+  return SA_OK;
+}
+
+float resolve_scale(const sa_desc* d) {
+  return d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->head_dim);
+}
+
+sa_status from_hip(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
+
+}  // namespace
+
+SA_EXPORT int32_t sparse_attn_abi_version(void) { return SPARSE_ATTN_ABI_VERSION; }
+
+SA_EXPORT const char* sparse_attn_status_string(sa_status st) {
+  switch (st) {
+    case SA_OK: return "ok";
+    case SA_ERR_NULL: return "a required pointer is NULL";
+    case SA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case SA_ERR_DTYPE: return "unknown dtype";
+    case SA_ERR_PARAM: return "alpha, density, select_mode, scale or a flag is out of range";
+    case SA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case SA_ERR_UNSUPPORTED: return "unsupported head_dim, block or number of blocks";
+    case SA_ERR_HIP: return "the HIP runtime reported an error";
+  }
+  return "unknown status";
+}
+
+SA_EXPORT sa_status sparse_attn_buffer_sizes(const sa_desc* desc, sa_sizes* sizes) {
+  sa::Shape s;
+  const sa_status st = check_desc(desc, &s);
+  if (st != SA_OK) return st;
+  if (!sizes) return SA_ERR_NULL;
+  const size_t f = sizeof(float);
+  sizes->q_bar = (size_t)s.B * s.Hq * s.M * s.D * f;
+  sizes->k_bar = (size_t)s.B * s.Hkv * s.M * s.D * f;
+  sizes->v_sum = desc->approx ? sizes->k_bar : 0;
+  sizes->blk_idx = (size_t)s.B * s.Hq * s.M * s.M * sizeof(int32_t);
+  sizes->blk_cnt = (size_t)s.B * s.Hq * s.M * sizeof(int32_t);
+  return SA_OK;
+}
+
+SA_EXPORT sa_status sparse_attn_block_pool(const sa_desc* desc, const void* q, const void* k,
+                                           const void* v, float* q_bar, float* k_bar,
+                                           float* v_sum, void* stream) {
+  sa::Shape s;
+  const sa_status st = check_desc(desc, &s);
+  if (st != SA_OK) return st;
+  if (!q || !k || !q_bar || !k_bar) return SA_ERR_NULL;
+  if (desc->approx && (!v || !v_sum)) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_bar) || !aligned16(k_bar)) return SA_ERR_ALIGN;
+  if (desc->approx && (!aligned16(v) || !aligned16(v_sum))) return SA_ERR_ALIGN;
+  return from_hip(sa::launch_pool(s, q, k, desc->approx ? v : nullptr, q_bar, k_bar,
+                                  desc->approx ? v_sum : nullptr, (hipStream_t)stream));
+}
+
+SA_EXPORT sa_status sparse_attn_select(const sa_desc* desc, const float* q_bar, const float* k_bar,
+                                       int32_t* blk_idx, int32_t* blk_cnt, void* stream) {
+  sa::Shape s;
+  const sa_status st = check_desc(desc, &s);
+  if (st != SA_OK) return st;
+  if (!q_bar || !k_bar || !blk_idx || !blk_cnt) return SA_ERR_NULL;
+  if (!aligned16(q_bar) || !aligned16(k_bar) || !aligned16(blk_idx) || !aligned16(blk_cnt))
+    return SA_ERR_ALIGN;
+  sa::SelectParams p;
+  p.scale = resolve_scale(desc);
+  p.mode = desc->select_mode;
+  p.alpha = (float)desc->alpha;
+  p.density = desc->density;
+  p.causal = desc->causal;
+  p.force_diag = desc->causal && desc->approx;
+  return from_hip(sa::launch_select(s, p, q_bar, k_bar, blk_idx, blk_cnt, (hipStream_t)stream));
+}
+
+SA_EXPORT sa_status sparse_attn_fwd(const sa_desc* desc, const void* q, const void* k, const void* v,
+                                    const float* k_bar, const float* v_sum, const int32_t* blk_idx,
+                                    const int32_t* blk_cnt, void* out, void* stream) {
+  sa::Shape s;
+  const sa_status st = check_desc(desc, &s);
+  if (st != SA_OK) return st;
+  if (!q || !k || !v || !blk_idx || !blk_cnt || !out) return SA_ERR_NULL;
+  if (desc->approx && (!k_bar || !v_sum)) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(blk_idx) ||
+      !aligned16(blk_cnt))
+    return SA_ERR_ALIGN;
+  if (desc->approx && (!aligned16(k_bar) || !aligned16(v_sum))) return SA_ERR_ALIGN;
+  sa::FwdParams p;
+  p.scale = resolve_scale(desc);
+  p.causal = desc->causal;
+  p.approx = desc->approx;
+  return from_hip(sa::launch_fwd(s, p, q, k, v, desc->approx ? k_bar : nullptr,
+                                 desc->approx ? v_sum : nullptr, blk_idx, blk_cnt, out,
+                                 (hipStream_t)stream));
+}

@@ -1,0 +1,44 @@
+// Internal host-side launch interface between the C ABI (api.cpp) and the
+// kernel translation units.  Not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+struct Shape {
+  int B, Hq, Hkv, N, D, block, M;
+  int dtype;  // 0 = f32, 1 = bf16
+};
+
+// Stage 1: block means of q and k, block sums of v (v may be null).
+hipError_t launch_pool(const Shape& s, const void* q, const void* k, const void* v,
+                       float* q_bar, float* k_bar, float* v_sum, hipStream_t st);
+
+// Stage 2: pooled scores + selection + compaction.
+struct SelectParams {
+  float scale;
+  int mode;        // 0 alpha, 1 density
+  float alpha;
+  double density;
+  int causal;
+  int force_diag;  // causal && approx
+};
+hipError_t launch_select(const Shape& s, const SelectParams& p, const float* q_bar,
+                         const float* k_bar, int32_t* blk_idx, int32_t* blk_cnt, hipStream_t st);
+
+// Stage 3: attention over the listed blocks (+ 0th-order tail).
+struct FwdParams {
+  float scale;
+  int causal;
+  int approx;
+};
+hipError_t launch_fwd(const Shape& s, const FwdParams& p, const void* q, const void* k,
+                      const void* v, const float* k_bar, const float* v_sum,
+                      const int32_t* blk_idx, const int32_t* blk_cnt, void* out, hipStream_t st);
+
+// Largest number of key blocks per row the selection kernel supports.
+constexpr int kMaxBlocks = 2048;
+
+}  // namespace sa

@@ -1,0 +1,160 @@
+/*
+ * sparse_attn.h -- C ABI of the gfx950 (MI355X) block-sparse attention library
+ * with pooled block routing.
+ *
+ * The method (three calls, one per stage):
+ *
+ *   1. sparse_attn_block_pool: cut the N tokens into M = ceil(N/block)
+ *      contiguous blocks; per block take the mean query, the mean key and
+ *      the sum of the values.  (PISA explainer, kodorricoding.tistory.com/108,
+ *      section "how candidate blocks are narrowed" and its routing table;
+ *      FlashPrefill summary, gist.science/ko/paper/2603.06199, technical
+ *      summary 2(a) "block approximation": average-pooled keys.)
+ *
+ *   2. sparse_attn_select: score every (query block I, key block J) pair
+ *      with the scaled pooled logit s_IJ = scale * qbar_I . kbar_J and keep,
+ *      per query block, either every J with s_IJ >= alpha * max_J s_IJ
+ *      (FlashPrefill summary 2(b), max-based dynamic threshold, no sort) or
+ *      the top-k blocks at a given density (PISA explainer, "minimal
+ *      documented usage": density=0.15, block_size=64).  The kept blocks are
+ *      written as ascending index lists (FlashPrefill summary 2(c):
+ *      index-driven jumping to the selected block coordinates).
+ *
+ *   3. sparse_attn_fwd: exact softmax attention over the tokens of the
+ *      listed blocks, with the running max / sum recurrence of the
+ *      FlashAttention tutorial (blog.mna-game.duckdns.org post 22, section 2,
+ *      online softmax equation).  With approx=1 every eligible block that is
+ *      not listed enters the same running max and sum as one pseudo-key
+ *      kbar_J of multiplicity n_J carrying the value sum SigmaV_J -- the
+ *      0th-order term exp(q.kbar_J) * (SigmaV_J, n_J) (PISA explainer, routing
+ *      table and section "why softmax survives approximating unselected
+ *      blocks").  The first-order global-statistic correction mentioned on
+ *      the same page is not implemented (the page does not define it).
+ *
+ * Readings where the pages are silent (both this library and its test oracle
+ * follow them):
+ *   - scale defaults to 1/sqrt(head_dim) for token and pooled logits;
+ *   - alpha mode: if a row's max score m is not positive the threshold is m
+ *     itself (only the arg-max blocks are kept); a score equal to the
+ *     threshold is kept;
+ *   - density mode: k = ceil(density * |E_I| - 1e-9) evaluated in double,
+ *     clamped to [1, |E_I|]; equal scores are taken in ascending J;
+ *   - causal: key block J is eligible for query block I iff J <= I; inside
+ *     the diagonal block a key j is visible to query i iff j <= i.  With
+ *     causal=1 and approx=1 the diagonal block is always exact (added to the
+ *     list by sparse_attn_select), since its pooled key would mix in later
+ *     tokens; the tail covers the unlisted J < I;
+ *   - Q head h reads KV head h / (heads_q / heads_kv) (consecutive grouping);
+ *   - the last block may be short (n_J < block); pooled means divide by n_J.
+ *
+ * Data layout (all tensors dense, row-major, 16-byte aligned device memory):
+ *   q    [batch, heads_q,  seq_len, head_dim]   element type = dtype
+ *   k, v [batch, heads_kv, seq_len, head_dim]   element type = dtype
+ *   out  [batch, heads_q,  seq_len, head_dim]   element type = dtype
+ *   q_bar [batch, heads_q,  M, head_dim] float32  (block means of q)
+ *   k_bar [batch, heads_kv, M, head_dim] float32  (block means of k)
+ *   v_sum [batch, heads_kv, M, head_dim] float32  (block sums of v)
+ *   blk_idx [batch, heads_q, M, M] int32: row (b,h,I) holds blk_cnt[b,h,I]
+ *           strictly ascending eligible key-block indices; entries past the
+ *           count are not read or written
+ *   blk_cnt [batch, heads_q, M] int32, 1 <= count <= M
+ *
+ * Ownership and threading: the caller allocates and frees every buffer
+ * (sizes from sparse_attn_buffer_sizes).  The library never allocates, frees
+ * or synchronises, keeps no state between calls and is reentrant.  Each
+ * compute call validates its arguments on the host, then enqueues kernels on
+ * the caller's HIP stream (`stream`, a hipStream_t; NULL = default stream)
+ * and returns without waiting.
+ *
+ * Errors: argument errors return a non-zero sa_status before anything is
+ * enqueued.  SA_ERR_HIP means a launch reported an error (hipGetLastError).
+ * Faults inside a kernel surface at the caller's next synchronisation.
+ * Caller-supplied block lists (sparse_attn_fwd) must satisfy the layout
+ * above; they are not checked on the host.
+ *
+ * Supported: head_dim in {64, 128}; block in {64, 128}; M <= 2048;
+ * dtype float32 or bfloat16; heads_q a multiple of heads_kv.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPARSE_ATTN_ABI_VERSION 1
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_NULL = 1,         /* a required pointer is NULL                          */
+  SA_ERR_SHAPE = 2,        /* a size is out of range or inconsistent               */
+  SA_ERR_DTYPE = 3,        /* dtype is not SA_DTYPE_F32 / SA_DTYPE_BF16             */
+  SA_ERR_PARAM = 4,        /* alpha / density / select_mode / flags out of range   */
+  SA_ERR_ALIGN = 5,        /* a tensor pointer is not 16-byte aligned              */
+  SA_ERR_UNSUPPORTED = 6,  /* valid in principle, not built (head_dim, block, M)   */
+  SA_ERR_HIP = 7           /* the HIP runtime reported an error at launch          */
+} sa_status;
+
+enum { SA_DTYPE_F32 = 0, SA_DTYPE_BF16 = 1 };
+enum { SA_SELECT_ALPHA = 0, SA_SELECT_DENSITY = 1 };
+
+typedef struct {
+  int32_t batch;        /* B >= 1                                            */
+  int32_t heads_q;      /* Hq >= 1                                           */
+  int32_t heads_kv;     /* Hkv >= 1, Hq % Hkv == 0                           */
+  int32_t seq_len;      /* N >= 1                                            */
+  int32_t head_dim;     /* d: 64 or 128                                      */
+  int32_t block;        /* b: tokens per block, 64 or 128                    */
+  int32_t dtype;        /* SA_DTYPE_F32 or SA_DTYPE_BF16 (q, k, v, out)      */
+  int32_t select_mode;  /* SA_SELECT_ALPHA or SA_SELECT_DENSITY              */
+  double alpha;         /* alpha mode: 0 < alpha <= 1                        */
+  double density;       /* density mode: 0 < density <= 1                    */
+  float scale;          /* logit scale; <= 0 selects 1/sqrt(head_dim)        */
+  int32_t causal;       /* 0 or 1                                            */
+  int32_t approx;       /* 0 or 1: fold unselected blocks in as 0th order    */
+} sa_desc;
+
+typedef struct {        /* bytes of each caller-allocated buffer */
+  size_t q_bar, k_bar, v_sum, blk_idx, blk_cnt;
+} sa_sizes;
+
+/* Bytes needed for the intermediate buffers of `desc` (host only, no GPU).
+ * v_sum is 0 when approx == 0.  Errors: SA_ERR_NULL, SA_ERR_SHAPE,
+ * SA_ERR_DTYPE, SA_ERR_PARAM, SA_ERR_UNSUPPORTED. */
+sa_status sparse_attn_buffer_sizes(const sa_desc* desc, sa_sizes* sizes);
+
+/* Stage 1, block pooling: one pass over q, k (and v when approx) writing
+ * q_bar, k_bar (block means) and v_sum (block sums), float32.  v and v_sum
+ * may be NULL when approx == 0 (then they are ignored). */
+sa_status sparse_attn_block_pool(const sa_desc* desc, const void* q, const void* k,
+                                 const void* v, float* q_bar, float* k_bar, float* v_sum,
+                                 void* stream);
+
+/* Stage 2, scoring + selection: pooled scores (float32, never stored),
+ * alpha-threshold or top-k selection, compaction into blk_idx / blk_cnt. */
+sa_status sparse_attn_select(const sa_desc* desc, const float* q_bar, const float* k_bar,
+                             int32_t* blk_idx, int32_t* blk_cnt, void* stream);
+
+/* Stage 3, attention: exact online-softmax attention over the listed blocks
+ * (+ the 0th-order tail over unlisted eligible blocks when approx == 1),
+ * output in dtype.  k_bar / v_sum may be NULL when approx == 0.  The lists
+ * may come from sparse_attn_select or from the caller (e.g. every eligible
+ * block for dense attention). */
+sa_status sparse_attn_fwd(const sa_desc* desc, const void* q, const void* k, const void* v,
+                          const float* k_bar, const float* v_sum, const int32_t* blk_idx,
+                          const int32_t* blk_cnt, void* out, void* stream);
+
+/* Static, human-readable text of a status code. */
+const char* sparse_attn_status_string(sa_status status);
+
+/* SPARSE_ATTN_ABI_VERSION of the loaded library. */
+int32_t sparse_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

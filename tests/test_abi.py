@@ -1,0 +1,132 @@
+"""C ABI: the built library loads, exports every function the header declares,
+and validates descriptors on the host (no GPU work is started here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_08_amd as bsa
+from block_sparse_attention_08_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                               reason="libsparse_attn.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_stages():
+    names = _declared()
+    for n in ("sparse_attn_block_pool", "sparse_attn_select", "sparse_attn_fwd",
+              "sparse_attn_buffer_sizes", "sparse_attn_status_string"):
+        assert n in names
+
+
+def test_struct_layout_matches_header():
+    # int32 x8, double x2, float, int32 x2 -> 64 bytes with natural alignment
+    assert ctypes.sizeof(_lib.SaDesc) == 64
+    assert _lib.SaDesc.alpha.offset == 32 and _lib.SaDesc.scale.offset == 48
+    assert ctypes.sizeof(_lib.SaSizes) == 5 * ctypes.sizeof(ctypes.c_size_t)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    h = _lib.lib()
+    for name in _declared():
+        assert hasattr(h, name), name
+    assert bsa.abi_version() == 1
+
+
+@needs_lib
+def test_status_strings():
+    h = _lib.lib()
+    for code in range(8):
+        s = h.sparse_attn_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert h.sparse_attn_status_string(99).decode() == "unknown status"
+
+
+def _desc(**kw):
+    base = dict(B=1, Hq=24, Hkv=24, N=8192, d=128, block=64, dtype="bf16", density=0.15,
+                causal=False, approx=True)
+    base.update(kw)
+    B, Hq, Hkv, N, d = base.pop("B"), base.pop("Hq"), base.pop("Hkv"), base.pop("N"), base.pop("d")
+    return bsa.make_desc(B, Hq, Hkv, N, d, **base)
+
+
+@needs_lib
+def test_buffer_sizes_image_workload():
+    s = bsa.buffer_sizes(_desc())
+    M = 128
+    assert s["q_bar"] == 24 * M * 128 * 4
+    assert s["k_bar"] == 24 * M * 128 * 4
+    assert s["v_sum"] == 24 * M * 128 * 4
+    assert s["blk_idx"] == 24 * M * M * 4
+    assert s["blk_cnt"] == 24 * M * 4
+    s0 = bsa.buffer_sizes(_desc(approx=False, N=32760))
+    assert s0["v_sum"] == 0 and s0["blk_cnt"] == 24 * 512 * 4
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=6, Hkv=4), 2),
+    (dict(N=0), 2),
+    (dict(d=96), 6),
+    (dict(block=32), 6),
+    (dict(N=2049 * 64), 6),          # more than 2048 blocks
+    (dict(density=1.5), 4),
+    (dict(density=0.0), 4),
+    (dict(density=None, alpha=0.0), 4),
+    (dict(density=None, alpha=1.01), 4),
+])
+def test_descriptor_validation(kw, code):
+    with pytest.raises(bsa.SparseAttnError) as e:
+        bsa.buffer_sizes(_desc(**kw))
+    assert e.value.status == code
+
+
+@needs_lib
+def test_bad_dtype_and_flags():
+    d = _desc()
+    d.dtype = 7
+    with pytest.raises(bsa.SparseAttnError) as e:
+        bsa.buffer_sizes(d)
+    assert e.value.status == 3
+    d = _desc()
+    d.causal = 2
+    with pytest.raises(bsa.SparseAttnError) as e:
+        bsa.buffer_sizes(d)
+    assert e.value.status == 4
+    d = _desc()
+    d.scale = float("nan")
+    with pytest.raises(bsa.SparseAttnError) as e:
+        bsa.buffer_sizes(d)
+    assert e.value.status == 4
+
+
+@needs_lib
+def test_compute_calls_reject_null_pointers_before_launch():
+    h = _lib.lib()
+    d = _desc()
+    assert h.sparse_attn_block_pool(d, None, None, None, None, None, None, None) == 1
+    assert h.sparse_attn_select(d, None, None, None, None, None) == 1
+    assert h.sparse_attn_fwd(d, None, None, None, None, None, None, None, None, None) == 1
+    assert h.sparse_attn_buffer_sizes(None, None) == 1
+    # misaligned (never dereferenced: validation returns first)
+    bad = ctypes.c_void_p(0x1003)
+    assert h.sparse_attn_select(d, bad, bad, bad, bad, None) == 5
+
+
+def test_make_desc_needs_exactly_one_rule():
+    with pytest.raises(ValueError):
+        bsa.make_desc(1, 1, 1, 64, 64, block=64, dtype="bf16")
+    with pytest.raises(ValueError):
+        bsa.make_desc(1, 1, 1, 64, 64, block=64, dtype="bf16", alpha=0.5, density=0.1)
