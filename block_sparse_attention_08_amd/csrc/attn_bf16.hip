@@ -28,15 +28,18 @@
 // The running max is only moved (and O, l rescaled) when a row's max grows
 // by more than 8 in log2 units, so p <= 256 and most tiles skip the rescale.
 //
-// K/V tiles travel HBM -> LDS with global_load_lds_dwordx4 (no registers).
-// Each wave instruction fills 1 KB of LDS contiguously, so every lane picks
-// the global 16-byte chunk that belongs at its LDS slot: the LDS tiles are
-// row-major with 16-byte chunks XOR-swizzled (K: chunk ^ (row & 7); V:
-// chunk ^ 2*(row & 3)), which keeps the MFMA operand reads free of bank
-// conflicts without padding.  One K buffer and one V buffer per workgroup;
-// the next K tile loads while this tile's softmax and PV run, the next V
-// tile while the next S runs (two barriers per tile).  Tail tiles come from
-// the float32 pooled K-bar / V-sum and are converted through registers.
+// K/V tiles travel HBM -> LDS with buffer_load_dwordx4 ... lds (no
+// registers), through buffer resources whose range check returns zero past
+// the last key.  Each wave instruction fills 1 KB of LDS contiguously, so
+// every lane picks the global 16-byte chunk that belongs at its LDS slot:
+// the LDS tiles are row-major with 16-byte chunks XOR-swizzled by row, which
+// keeps the MFMA operand reads free of bank conflicts without padding.
+// 128-row query blocks double-buffer K and V and software-pipeline: S of
+// tile e+1 sits next to the softmax of tile e, one barrier per tile.
+// 64-row blocks keep one K and one V buffer (four workgroups per CU): the
+// next K tile loads during this tile's softmax and PV, the next V tile
+// during the next S (two barriers per tile).  Tail tiles come from the
+// float32 pooled K-bar / V-sum and are converted through registers.
 // Workgroups are ordered so that each XCD receives a contiguous range of
 // (kv head, query block) items, with the query heads of one KV group
 // adjacent, so K/V blocks shared by neighbouring items stay in one L2.
@@ -90,8 +93,18 @@ struct Cfg {
   static_assert(NI >= 1, "tile smaller than the workgroup");
 };
 
-__device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & 7); }
-__device__ __forceinline__ int v_chunk(int r, int c) { return c ^ ((r & 3) << 1); }
+// LDS swizzles of the 16-byte chunks of a tile row (free of bank conflicts
+// for the MFMA operand reads whether the LDS serves 128 or 256 bytes a clock):
+// K rows: chunk ^ (row & 15) (d = 128) or chunk ^ (row & 7) (d = 64);
+// V rows: chunk ^ {0, 4, 10, 14}[row & 3] (d = 128) or chunk ^ 2*(row & 3).
+template <int D>
+__device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & (D == 128 ? 15 : 7)); }
+template <int D>
+__device__ __forceinline__ int v_chunk(int r, int c) {
+  return D == 128 ? c ^ (((r & 3) << 2) | (r & 2)) : c ^ ((r & 3) << 1);
+}
+
+constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
@@ -102,17 +115,26 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Byte offset, inside a KT x D tile, of the global 16-byte chunk this lane
-// copies with every direct load: instruction i of wave w fills LDS chunks
-// (i*NW + w)*64 + lane, i.e. rows advance by whole KB per instruction and,
-// since NW*64/CPR rows is a multiple of 8, the swizzle of a lane's row is
-// the same for every i.  So instruction i reads lane_off + i*NW*1024.
+// copies with direct load i: instruction i of wave w fills LDS chunks
+// (i*NW + w)*64 + lane, so rows advance by whole KB per instruction and the
+// lane's swizzle repeats with period NVAR in i (the swizzle period in rows
+// over the rows per KB, divided by the waves).  Instruction i reads
+// lane_off[i % NVAR] + i*NW*1024.
+template <int D, int BLK>
+struct DmaCfg {
+  static constexpr int ROWS_PER_KB = 1024 / (2 * D);
+  static constexpr int PERIOD = D == 128 ? 16 : 8;            // K swizzle period in rows
+  static constexpr int STEP = Cfg<D, BLK>::NW * ROWS_PER_KB;  // rows per instruction step
+  static constexpr int NVAR = STEP % PERIOD == 0 ? 1 : PERIOD / STEP;
+};
+
 template <int D, int BLK, bool IS_V>
-__device__ __forceinline__ int dma_lane_off(int w, int lane) {
+__device__ __forceinline__ int dma_lane_off(int i, int w, int lane) {
   using C = Cfg<D, BLK>;
-  const int P = w * 64 + lane;
+  const int P = (i * C::NW + w) * 64 + lane;
   const int r = P / C::CPR, pc = P % C::CPR;
-  const int c = IS_V ? v_chunk(r, pc) : k_chunk(r, pc);
-  return r * C::ROWB + c * 16;
+  const int c = IS_V ? v_chunk<D>(r, pc) : k_chunk<D>(r, pc);
+  return (r - i * C::NW * DmaCfg<D, BLK>::ROWS_PER_KB) * C::ROWB + c * 16;
 }
 
 // Buffer resource over one K or V head ([N, D] bf16): loads past its last
@@ -126,12 +148,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base
 // `tile_off` of the head.
 template <int D, int BLK>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int tile_off, char* lds, int w,
-                                         int lane_off) {
+                                         const int (&lane_off)[DmaCfg<D, BLK>::NVAR]) {
   using C = Cfg<D, BLK>;
 #pragma unroll
   for (int i = 0; i < C::NI; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (i * C::NW + w) * 1024), 16,
-                                             lane_off, tile_off + i * C::NW * 1024, 0, 0);
+                                             lane_off[i % DmaCfg<D, BLK>::NVAR],
+                                             tile_off + i * C::NW * 1024, 0, 0);
 }
 
 // Tail tile: float32 pooled rows -> bf16 -> the same swizzled LDS layout.
@@ -147,7 +170,7 @@ __device__ __forceinline__ void reg_tile(const float* src, char* lds, int valid,
     const int P = (i * C::NW + w) * 64 + lane;
     const int r = P / C::CPR;
     const int pc = P % C::CPR;
-    const int c = IS_V ? v_chunk(r, pc) : k_chunk(r, pc);
+    const int c = IS_V ? v_chunk<D>(r, pc) : k_chunk<D>(r, pc);
     u32x4 x = {0u, 0u, 0u, 0u};
     if (r < valid) {
       f32x4 lo = *reinterpret_cast<const f32x4*>(src + (size_t)r * D + 8 * c);
@@ -202,12 +225,30 @@ __device__ __forceinline__ void mask_tail(f32x16 (&s)[2], int lim, uint32_t w0, 
   }
 }
 
-// Online softmax + PV for one 64-key tile (S^T accumulators s[0], s[1],
-// already masked): running max with lazy rescale, exp2, bf16 pack, and
-// O^T += V^T P^T with V^T read by LDS transpose loads.
+// V^T operand of PV step (nt, kc): two LDS transpose reads.
 template <int D, int BLK>
-__device__ __forceinline__ void softmax_pv(State<D, BLK>& st, f32x16 (&s)[2], const char* Vs,
-                                           const int (&vbase)[Cfg<D, BLK>::NOT], float c) {
+__device__ __forceinline__ bf16x8 v_operand(const char* Vs, const int (&vbase)[Cfg<D, BLK>::NOT], int nt, int kc) {
+  using C = Cfg<D, BLK>;
+  const char* p = Vs + vbase[nt] + (16 * kc) * C::ROWB;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * C::ROWB));
+  return __builtin_bit_cast(
+      bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
+// K operand of S step (js, ks).
+template <int D, int BLK>
+__device__ __forceinline__ bf16x8 k_operand(const char* Ks, const int (&kbase)[Cfg<D, BLK>::NKS], int step) {
+  using C = Cfg<D, BLK>;
+  const int js = step / C::NKS, ks = step % C::NKS;
+  return *reinterpret_cast<const bf16x8*>(Ks + kbase[ks] + 32 * js * C::ROWB);
+}
+
+// Online softmax, part 1, for one 64-key tile (S^T accumulators s[0], s[1],
+// already masked): running max with lazy rescale of O and l.  Returns the
+// reference max (0 while no key has been seen) for the exponentials.
+template <int D, int BLK>
+__device__ __forceinline__ float softmax_max(State<D, BLK>& st, const f32x16 (&s)[2], float c) {
   using C = Cfg<D, BLK>;
   float mx = -INFINITY;
 #pragma unroll
@@ -228,8 +269,16 @@ __device__ __forceinline__ void softmax_pv(State<D, BLK>& st, f32x16 (&s)[2], co
     }
     st.m = m_new;
   }
-  const float mb = st.m == -INFINITY ? 0.f : st.m;
+  return st.m == -INFINITY ? 0.f : st.m;
+}
 
+// Online softmax, part 2: P = exp2(S*c - mb) packed to bf16, row sums of
+// the packed values (dot2 with ones), and O^T += V^T P^T with V^T read by
+// LDS transpose loads.
+template <int D, int BLK>
+__device__ __forceinline__ void softmax_pv(State<D, BLK>& st, const f32x16 (&s)[2], const char* Vs,
+                                           const int (&vbase)[Cfg<D, BLK>::NOT], float c, float mb) {
+  using C = Cfg<D, BLK>;
   bf16x8 pk[4];
   float lsum = 0.f;
 #pragma unroll
@@ -242,33 +291,125 @@ __device__ __forceinline__ void softmax_pv(State<D, BLK>& st, f32x16 (&s)[2], co
         const int r0 = 8 * h2 + 2 * q2;
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[js][r0], c, -mb));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[js][r0 + 1], c, -mb));
-        lsum += p0 + p1;
         wd[q2] = pack2(p0, p1);
+        // row sum of the bf16-rounded P that the PV product uses
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[q2]), kOnes, lsum, false);
       }
       pk[2 * js + h2] = __builtin_bit_cast(bf16x8, u32x4{wd[0], wd[1], wd[2], wd[3]});
     }
   }
   st.l += lsum;
 
+  constexpr int VD = 4;
+  constexpr int NPV = 4 * C::NOT;
+  bf16x8 vr[VD];
 #pragma unroll
-  for (int nt = 0; nt < C::NOT; ++nt) {
+  for (int j = 0; j < VD; ++j) vr[j] = v_operand<D, BLK>(Vs, vbase, j / 4, j % 4);
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const char* p = Vs + vbase[nt] + (16 * kc) * C::ROWB;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * C::ROWB));
-      const bf16x8 va = __builtin_bit_cast(
-          bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-      st.o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[kc], st.o[nt], 0, 0, 0);
+  for (int j = 0; j < NPV; ++j) {
+    const bf16x8 va = vr[j % VD];
+    if (j + VD < NPV) vr[j % VD] = v_operand<D, BLK>(Vs, vbase, (j + VD) / 4, (j + VD) % 4);
+    st.o[j / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[j % 4], st.o[j / 4], 0, 0, 0);
+  }
+}
+
+// S^T = K Q^T for one 64-key tile held in LDS (K operands read 3 ahead).
+template <int D, int BLK>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const char* Ks, const int (&kbase)[Cfg<D, BLK>::NKS],
+                                        const bf16x8 (&qf)[Cfg<D, BLK>::NKS]) {
+  using C = Cfg<D, BLK>;
+  constexpr int NSTEP = 2 * C::NKS;
+  constexpr int KD = 3;
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+  bf16x8 kr[KD];
+#pragma unroll
+  for (int i = 0; i < KD; ++i) kr[i] = k_operand<D, BLK>(Ks, kbase, i);
+#pragma unroll
+  for (int step = 0; step < NSTEP; ++step) {
+    const bf16x8 ka = kr[step % KD];
+    if (step + KD < NSTEP) kr[step % KD] = k_operand<D, BLK>(Ks, kbase, step + KD);
+    s[step / C::NKS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[step % C::NKS], s[step / C::NKS], 0, 0, 0);
+  }
+}
+
+// Pipelined tile step: S^T of the next tile (one MFMA per step) interleaved
+// with the exponentials of this tile, then O^T += V^T P^T.  LDS operands are
+// read ahead through small register rings (K three steps ahead; the first V
+// operands during the last S steps, then four ahead), and a scheduling
+// barrier between steps keeps the compiler from regrouping the
+// exponentials ahead of the products, so the matrix cores and the vector
+// ALUs work side by side.
+template <int D, int BLK>
+__device__ __forceinline__ void pipe_step(State<D, BLK>& st, const f32x16 (&s)[2], f32x16 (&s_next)[2],
+                                          const char* Ks_next, const char* Vs,
+                                          const int (&kbase)[Cfg<D, BLK>::NKS],
+                                          const int (&vbase)[Cfg<D, BLK>::NOT],
+                                          const bf16x8 (&qf)[Cfg<D, BLK>::NKS], float c, float mb) {
+  using C = Cfg<D, BLK>;
+  constexpr int NSTEP = 2 * C::NKS;          // S MFMAs of one 64-key tile
+  constexpr int PER = 16 / NSTEP;            // element pairs per step (1, or 2 for d = 64)
+  static_assert(PER * NSTEP == 16, "16 element pairs (32 scores) per lane and tile");
+  constexpr int KD = 3;                      // K operand ring depth
+  constexpr int VD = 4;                      // V operand ring depth
+  constexpr int NPV = 4 * C::NOT;            // PV MFMAs of one tile
+  uint32_t wd[16];
+  float lsum = 0.f;
+  s_next[0] = f32x16{};
+  s_next[1] = f32x16{};
+  bf16x8 kr[KD];
+#pragma unroll
+  for (int i = 0; i < KD; ++i) kr[i] = k_operand<D, BLK>(Ks_next, kbase, i);
+  bf16x8 vr[VD];
+#pragma unroll
+  for (int step = 0; step < NSTEP; ++step) {
+    const int js = step / C::NKS, ks = step % C::NKS;
+    const bf16x8 ka = kr[step % KD];
+    if (step + KD < NSTEP) kr[step % KD] = k_operand<D, BLK>(Ks_next, kbase, step + KD);
+    const int vi = step - (NSTEP - VD);      // start the V operands in the last steps
+    if (vi >= 0) vr[vi] = v_operand<D, BLK>(Vs, vbase, vi / 4, vi % 4);
+    s_next[js] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s_next[js], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = step * PER + u;          // element pair 0..15
+      const int ej = q >> 3, r0 = 2 * (q & 7);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ej][r0], c, -mb));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[ej][r0 + 1], c, -mb));
+      wd[q] = pack2(p0, p1);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[q]), kOnes, lsum, false);
+      // an empty volatile statement using the packed pair: keeps its
+      // computation inside this step (pure arithmetic would otherwise be
+      // moved past the scheduling barrier)
+      asm volatile("" ::"v"(wd[q]));
     }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.l += lsum;
+  // pair q = 8*ej + (r0/2) holds keys of sub-tile ej, registers r0, r0+1;
+  // PV step kc = 2*ej + h2 takes registers 8*h2 .. 8*h2 + 7 of sub-tile ej
+  bf16x8 pk[4];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    const int base = 8 * (kc >> 1) + 4 * (kc & 1);
+    pk[kc] = __builtin_bit_cast(bf16x8, u32x4{wd[base], wd[base + 1], wd[base + 2], wd[base + 3]});
+  }
+#pragma unroll
+  for (int j = 0; j < NPV; ++j) {
+    const bf16x8 va = vr[j % VD];
+    if (j + VD < NPV) vr[j % VD] = v_operand<D, BLK>(Vs, vbase, (j + VD) / 4, (j + VD) % 4);
+    st.o[j / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[j % 4], st.o[j / 4], 0, 0, 0);
   }
 }
 
 template <int D, int BLK>
 __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
   using C = Cfg<D, BLK>;
-  __shared__ __attribute__((aligned(1024))) char Ks[KT * D * 2];
-  __shared__ __attribute__((aligned(1024))) char Vs[KT * D * 2];
+  // K and V tile buffers: tile e uses buffer e % NBUF.  128-row query
+  // blocks double-buffer (software pipeline, one barrier per tile); 64-row
+  // blocks single-buffer, which keeps 4 two-wave workgroups per CU.
+  constexpr int NBUF = BLK == 128 ? 2 : 1;
+  __shared__ __attribute__((aligned(1024))) char Ks[NBUF][KT * D * 2];
+  __shared__ __attribute__((aligned(1024))) char Vs[NBUF][KT * D * 2];
   // one spare word: the tail mask reads the word after the tile's first
   __shared__ uint32_t selbits[kMaxBlocks / 32 + 1];
 
@@ -333,7 +474,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
   // V transpose-read bases (per 32-wide d tile); tile-invariant.
   int kbase[C::NKS];
 #pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) kbase[ks] = lq * C::ROWB + k_chunk(lq, 2 * ks + hh) * 16;
+  for (int ks = 0; ks < C::NKS; ++ks) kbase[ks] = lq * C::ROWB + k_chunk<D>(lq, 2 * ks + hh) * 16;
   int vbase[C::NOT];
   {
     const int i16 = lane & 15, grp = lane >> 4;
@@ -341,7 +482,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < C::NOT; ++nt) {
       const int n = 32 * nt + 16 * (grp & 1) + 4 * (i16 & 3);
-      vbase[nt] = jr * C::ROWB + v_chunk(jr, n >> 3) * 16 + (n & 7) * 2;
+      vbase[nt] = jr * C::ROWB + v_chunk<D>(jr, n >> 3) * 16 + (n & 7) * 2;
     }
   }
 
@@ -350,19 +491,25 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
     if (e < n_exact) return list[e / C::SUB] * BLK + (e % C::SUB) * KT;
     return (e - n_exact) * KT;
   };
-  const int koff = dma_lane_off<D, BLK, false>(w, lane);
-  const int voff = dma_lane_off<D, BLK, true>(w, lane);
+  int koff[DmaCfg<D, BLK>::NVAR], voff[DmaCfg<D, BLK>::NVAR];
+#pragma unroll
+  for (int i = 0; i < DmaCfg<D, BLK>::NVAR; ++i) {
+    koff[i] = dma_lane_off<D, BLK, false>(i, w, lane);
+    voff[i] = dma_lane_off<D, BLK, true>(i, w, lane);
+  }
   auto issue_k = [&](int e, int key0) {
+    char* buf = Ks[e % NBUF];
     if (e < n_exact)
-      dma_tile<D, BLK>(krs, key0 * C::ROWB, Ks, w, koff);
+      dma_tile<D, BLK>(krs, key0 * C::ROWB, buf, w, koff);
     else
-      reg_tile<D, BLK, false>(a.k_bar + pp_off + (size_t)key0 * D, Ks, a.M - key0, w, lane, 0, 0.f);
+      reg_tile<D, BLK, false>(a.k_bar + pp_off + (size_t)key0 * D, buf, a.M - key0, w, lane, 0, 0.f);
   };
   auto issue_v = [&](int e, int key0) {
+    char* buf = Vs[e % NBUF];
     if (e < n_exact)
-      dma_tile<D, BLK>(vrs, key0 * C::ROWB, Vs, w, voff);
+      dma_tile<D, BLK>(vrs, key0 * C::ROWB, buf, w, voff);
     else
-      reg_tile<D, BLK, true>(a.v_sum + pp_off + (size_t)key0 * D, Vs, a.M - key0, w, lane,
+      reg_tile<D, BLK, true>(a.v_sum + pp_off + (size_t)key0 * D, buf, a.M - key0, w, lane,
                              a.M - 1 - key0, 1.0f / (float)last_n);
   };
 
@@ -371,48 +518,78 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
   for (int i = 0; i < C::NOT; ++i) st.o[i] = f32x16{};
   st.m = -INFINITY;
   st.l = 0.f;
+  const float c = a.scale_log2;
 
-  int key0 = tile_key0(0);
-  issue_k(0, key0);
-  issue_v(0, key0);
-  wait_vm();
-  __syncthreads();
-
-  for (int e = 0; e < n_tiles; ++e) {
-    const bool pseudo = e >= n_exact;
-    // skip exact tiles that lie wholly past the last token (ragged last block)
-    const int next_key0 = e + 1 < n_tiles ? tile_key0(e + 1) : 0;
-
-    // ---- S^T = K Q^T
-    f32x16 s[2];
-#pragma unroll
-    for (int js = 0; js < 2; ++js) {
-      s[js] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < C::NKS; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + kbase[ks] + 32 * js * C::ROWB);
-        s[js] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[js], 0, 0, 0);
-      }
-    }
-    wait_vm();
-    __syncthreads();                 // K buffer free, V tile e landed in every wave
-    if (e + 1 < n_tiles) issue_k(e + 1, next_key0);
-
-    if (pseudo) {
+  // mask tile e in place (tail tiles: selection bits, eligibility and the
+  // multiplicity offset; exact tiles: end of sequence and causal diagonal)
+  auto mask_tile = [&](f32x16 (&sv)[2], int e, int key0) {
+    if (e >= n_exact) {
       const uint32_t w0 = selbits[key0 >> 5] >> (4 * hh);
       const uint32_t w1 = selbits[(key0 >> 5) + 1] >> (4 * hh);
-      mask_tail(s, Jend - key0 - 4 * hh, w0, w1, a.M - 1 - key0 - 4 * hh, bias_blk, bias_last);
+      mask_tail(sv, Jend - key0 - 4 * hh, w0, w1, a.M - 1 - key0 - 4 * hh, bias_blk, bias_last);
     } else if (key0 + KT > a.N || (a.causal && key0 + KT > I * BLK)) {
       int lim = a.N - key0;
       if (a.causal) lim = min(lim, q_tok - key0 + 1);
-      mask_exact(s, lim - 4 * hh);
+      mask_exact(sv, lim - 4 * hh);
     }
-    softmax_pv<D, BLK>(st, s, Vs, vbase, a.scale_log2);
+  };
 
+  if constexpr (NBUF == 2) {
+    // Pipeline: while the softmax of tile e runs on the vector ALUs, the
+    // matrix cores compute S of tile e+1; K e+2 and V e+1 load meanwhile.
+    // One barrier per tile: it retires tile e's buffers and publishes the
+    // loads issued during it.
+    int key0 = tile_key0(0);
+    int key1 = n_tiles > 1 ? tile_key0(1) : 0;
+    issue_k(0, key0);
+    issue_v(0, key0);
+    if (n_tiles > 1) issue_k(1, key1);
     wait_vm();
-    __syncthreads();                 // V buffer free, K tile e+1 landed in every wave
-    if (e + 1 < n_tiles) issue_v(e + 1, next_key0);
-    key0 = next_key0;
+    __syncthreads();
+    f32x16 s[2];
+    qk_tile<D, BLK>(s, Ks[0], kbase, qf);
+
+    for (int e = 0; e < n_tiles; ++e) {
+      const int cur = e & 1;
+      const int key2 = e + 2 < n_tiles ? tile_key0(e + 2) : 0;
+      if (e + 1 < n_tiles) issue_v(e + 1, key1);
+      if (e + 2 < n_tiles) issue_k(e + 2, key2);
+      mask_tile(s, e, key0);
+      const float mb = softmax_max<D, BLK>(st, s, c);
+      // S of tile e+1 (on the last tile this reads a retired buffer and the
+      // result is dropped) interleaved with the softmax of tile e
+      f32x16 s_next[2];
+      pipe_step<D, BLK>(st, s, s_next, Ks[cur ^ 1], Vs[cur], kbase, vbase, qf, c, mb);
+      wait_vm();
+      __syncthreads();
+#pragma unroll
+      for (int js = 0; js < 2; ++js) s[js] = s_next[js];
+      key0 = key1;
+      key1 = key2;
+    }
+  } else {
+    // Single buffers, two barriers per tile: K e+1 loads during the softmax
+    // and PV of tile e, V e+1 during S of tile e+1.
+    int key0 = tile_key0(0);
+    issue_k(0, key0);
+    issue_v(0, key0);
+    wait_vm();
+    __syncthreads();
+    for (int e = 0; e < n_tiles; ++e) {
+      const int key1 = e + 1 < n_tiles ? tile_key0(e + 1) : 0;
+      f32x16 s[2];
+      qk_tile<D, BLK>(s, Ks[0], kbase, qf);
+      wait_vm();
+      __syncthreads();                 // K buffer free, V tile e landed in every wave
+      if (e + 1 < n_tiles) issue_k(e + 1, key1);
+      mask_tile(s, e, key0);
+      const float mb = softmax_max<D, BLK>(st, s, c);
+      softmax_pv<D, BLK>(st, s, Vs[0], vbase, c, mb);
+      wait_vm();
+      __syncthreads();                 // V buffer free, K tile e+1 landed in every wave
+      if (e + 1 < n_tiles) issue_v(e + 1, key1);
+      key0 = key1;
+    }
   }
 
   // ---- epilogue: O / l, bf16, row q_tok; register r of d-tile nt holds

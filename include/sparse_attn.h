@@ -56,7 +56,9 @@
  *   v_sum [batch, heads_kv, M, head_dim] float32  (block sums of v)
  *   blk_idx [batch, heads_q, M, M] int32: row (b,h,I) holds blk_cnt[b,h,I]
  *           strictly ascending eligible key-block indices; entries past the
- *           count are not read or written
+ *           count are unspecified (sparse_attn_select uses the whole buffer
+ *           as scratch for the M x M block scores before compacting each
+ *           row in place; sparse_attn_fwd reads only the first count)
  *   blk_cnt [batch, heads_q, M] int32, 1 <= count <= M
  *
  * Ownership and threading: the caller allocates and frees every buffer
@@ -133,8 +135,9 @@ sa_status sparse_attn_block_pool(const sa_desc* desc, const void* q, const void*
                                  const void* v, float* q_bar, float* k_bar, float* v_sum,
                                  void* stream);
 
-/* Stage 2, scoring + selection: pooled scores (float32, never stored),
- * alpha-threshold or top-k selection, compaction into blk_idx / blk_cnt. */
+/* Stage 2, scoring + selection: pooled scores (float32, held in blk_idx as
+ * scratch), alpha-threshold or top-k selection, compaction of every row in
+ * place into blk_idx / blk_cnt. */
 sa_status sparse_attn_select(const sa_desc* desc, const float* q_bar, const float* k_bar,
                              int32_t* blk_idx, int32_t* blk_cnt, void* stream);
 
