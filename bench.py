@@ -177,16 +177,16 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record()
-        bsa.block_pool(desc, qd, kd, vd, ws.q_bar, ws.k_bar, ws.v_sum)
+        bsa.block_pool(desc, qd, kd, vd, ws.q_bar, ws.k_bar, ws.v_sum, ws.tail)
         if ev:
             ev[1].record()
         bsa.select(desc, ws.q_bar, ws.k_bar, ws.blk_idx, ws.blk_cnt)
         if ev:
             ev[2].record()
         if args.dense:
-            bsa.fwd(desc, qd, kd, vd, ws.k_bar, ws.v_sum, dense_idx, dense_cnt, out)
+            bsa.fwd(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, dense_idx, dense_cnt, out)
         else:
-            bsa.fwd(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.blk_idx, ws.blk_cnt, out)
+            bsa.fwd(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, ws.blk_idx, ws.blk_cnt, out)
         if ev:
             ev[3].record()
 

@@ -73,7 +73,9 @@ def _m(desc: SaDesc) -> int:
 
 class Workspace:
     """Caller-owned intermediates for one descriptor: pooled Q/K (float32),
-    V sums (float32, when the tail is on), block lists and counts (int32)."""
+    V sums (float32, when the tail is on), the bf16 tail operands (block
+    means of K and V, bf16 inputs with the tail on), block lists and counts
+    (int32)."""
 
     def __init__(self, desc: SaDesc, device="cuda"):
         import torch
@@ -84,15 +86,18 @@ class Workspace:
         self.q_bar = torch.empty((B, Hq, M, d), dtype=f32, device=device)
         self.k_bar = torch.empty((B, Hkv, M, d), dtype=f32, device=device)
         self.v_sum = torch.empty((B, Hkv, M, d), dtype=f32, device=device) if desc.approx else None
+        self.tail = (torch.empty((2, B, Hkv, M, d), dtype=torch.bfloat16, device=device)
+                     if sizes["tail"] else None)
         self.blk_idx = torch.empty((B, Hq, M, M), dtype=i32, device=device)
         self.blk_cnt = torch.empty((B, Hq, M), dtype=i32, device=device)
         assert self.q_bar.numel() * 4 == sizes["q_bar"] and self.blk_idx.numel() * 4 == sizes["blk_idx"]
 
 
-def block_pool(desc, q, k, v, q_bar, k_bar, v_sum, stream=None) -> None:
-    """Stage 1: block means of q and k, block sums of v (v_sum when approx)."""
+def block_pool(desc, q, k, v, q_bar, k_bar, v_sum, tail=None, stream=None) -> None:
+    """Stage 1: block means of q and k, block sums of v (v_sum when approx),
+    and the bf16 tail operands (bf16 inputs with approx)."""
     st = _lib.lib().sparse_attn_block_pool(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(q_bar),
-                                           _ptr(k_bar), _ptr(v_sum), _stream(stream))
+                                           _ptr(k_bar), _ptr(v_sum), _ptr(tail), _stream(stream))
     _lib.check(st, "sparse_attn_block_pool")
 
 
@@ -103,10 +108,12 @@ def select(desc, q_bar, k_bar, blk_idx, blk_cnt, stream=None) -> None:
     _lib.check(st, "sparse_attn_select")
 
 
-def fwd(desc, q, k, v, k_bar, v_sum, blk_idx, blk_cnt, out, stream=None) -> None:
-    """Stage 3: attention over the listed blocks (+ 0th-order tail when approx)."""
+def fwd(desc, q, k, v, k_bar, v_sum, tail, blk_idx, blk_cnt, out, stream=None) -> None:
+    """Stage 3: attention over the listed blocks (+ 0th-order tail when
+    approx: k_bar/v_sum for float32 inputs, tail for bf16 inputs)."""
     st = _lib.lib().sparse_attn_fwd(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(k_bar), _ptr(v_sum),
-                                    _ptr(blk_idx), _ptr(blk_cnt), _ptr(out), _stream(stream))
+                                    _ptr(tail), _ptr(blk_idx), _ptr(blk_cnt), _ptr(out),
+                                    _stream(stream))
     _lib.check(st, "sparse_attn_fwd")
 
 
@@ -146,9 +153,9 @@ def block_sparse_attention(q, k, v, *, block_size: int = 64, alpha: Optional[flo
     desc = ws.desc
     if out is None:
         out = torch.empty_like(q)
-    block_pool(desc, q, k, v, ws.q_bar, ws.k_bar, ws.v_sum)
+    block_pool(desc, q, k, v, ws.q_bar, ws.k_bar, ws.v_sum, ws.tail)
     select(desc, ws.q_bar, ws.k_bar, ws.blk_idx, ws.blk_cnt)
-    fwd(desc, q, k, v, ws.k_bar, ws.v_sum, ws.blk_idx, ws.blk_cnt, out)
+    fwd(desc, q, k, v, ws.k_bar, ws.v_sum, ws.tail, ws.blk_idx, ws.blk_cnt, out)
     if return_selection:
         return out, ws.blk_idx, ws.blk_cnt
     return out

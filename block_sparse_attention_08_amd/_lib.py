@@ -42,7 +42,7 @@ class SaDesc(ctypes.Structure):
 
 
 class SaSizes(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("q_bar", "k_bar", "v_sum", "blk_idx", "blk_cnt")]
+    _fields_ = [(n, ctypes.c_size_t) for n in ("q_bar", "k_bar", "v_sum", "tail", "blk_idx", "blk_cnt")]
 
 
 class SparseAttnError(ValueError):
@@ -57,9 +57,9 @@ _lock = threading.Lock()
 _P = ctypes.c_void_p
 _SIGS = {
     "sparse_attn_buffer_sizes": [ctypes.POINTER(SaDesc), ctypes.POINTER(SaSizes)],
-    "sparse_attn_block_pool": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P, _P, _P],
+    "sparse_attn_block_pool": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P, _P, _P, _P],
     "sparse_attn_select": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P],
-    "sparse_attn_fwd": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "sparse_attn_fwd": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "sparse_attn_status_string": [ctypes.c_int],
     "sparse_attn_abi_version": [],
 }

@@ -30,6 +30,7 @@ sa_status check_desc(const sa_desc* d, sa::Shape* s) {
   if (d->block != 64 && d->block != 128) return SA_ERR_UNSUPPORTED;
   const int M = (d->seq_len + d->block - 1) / d->block;
   if (M > sa::kMaxBlocks) return SA_ERR_UNSUPPORTED;
+  if ((int64_t)d->batch * d->heads_q > 65535) return SA_ERR_UNSUPPORTED;   // grid z of the score pass
   // every workgroup count and per-row index of the kernels is a 32-bit int
   const int64_t items = (int64_t)d->batch * (d->heads_q + 2 * (int64_t)d->heads_kv) * M;
   if (items > INT32_MAX / 2) return SA_ERR_SHAPE;
@@ -79,6 +80,7 @@ SA_EXPORT sa_status sparse_attn_buffer_sizes(const sa_desc* desc, sa_sizes* size
   sizes->q_bar = (size_t)s.B * s.Hq * s.M * s.D * f;
   sizes->k_bar = (size_t)s.B * s.Hkv * s.M * s.D * f;
   sizes->v_sum = desc->approx ? sizes->k_bar : 0;
+  sizes->tail = (desc->approx && desc->dtype == SA_DTYPE_BF16) ? 2 * (size_t)s.B * s.Hkv * s.M * s.D * 2 : 0;
   sizes->blk_idx = (size_t)s.B * s.Hq * s.M * s.M * sizeof(int32_t);
   sizes->blk_cnt = (size_t)s.B * s.Hq * s.M * sizeof(int32_t);
   return SA_OK;
@@ -86,16 +88,20 @@ SA_EXPORT sa_status sparse_attn_buffer_sizes(const sa_desc* desc, sa_sizes* size
 
 SA_EXPORT sa_status sparse_attn_block_pool(const sa_desc* desc, const void* q, const void* k,
                                            const void* v, float* q_bar, float* k_bar,
-                                           float* v_sum, void* stream) {
+                                           float* v_sum, void* tail, void* stream) {
   sa::Shape s;
   const sa_status st = check_desc(desc, &s);
   if (st != SA_OK) return st;
+  const bool need_tail = desc->approx && desc->dtype == SA_DTYPE_BF16;
   if (!q || !k || !q_bar || !k_bar) return SA_ERR_NULL;
   if (desc->approx && (!v || !v_sum)) return SA_ERR_NULL;
+  if (need_tail && !tail) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_bar) || !aligned16(k_bar)) return SA_ERR_ALIGN;
   if (desc->approx && (!aligned16(v) || !aligned16(v_sum))) return SA_ERR_ALIGN;
+  if (need_tail && !aligned16(tail)) return SA_ERR_ALIGN;
   return from_hip(sa::launch_pool(s, q, k, desc->approx ? v : nullptr, q_bar, k_bar,
-                                  desc->approx ? v_sum : nullptr, (hipStream_t)stream));
+                                  desc->approx ? v_sum : nullptr, need_tail ? tail : nullptr,
+                                  (hipStream_t)stream));
 }
 
 SA_EXPORT sa_status sparse_attn_select(const sa_desc* desc, const float* q_bar, const float* k_bar,
@@ -117,22 +123,27 @@ SA_EXPORT sa_status sparse_attn_select(const sa_desc* desc, const float* q_bar, 
 }
 
 SA_EXPORT sa_status sparse_attn_fwd(const sa_desc* desc, const void* q, const void* k, const void* v,
-                                    const float* k_bar, const float* v_sum, const int32_t* blk_idx,
-                                    const int32_t* blk_cnt, void* out, void* stream) {
+                                    const float* k_bar, const float* v_sum, const void* tail,
+                                    const int32_t* blk_idx, const int32_t* blk_cnt, void* out,
+                                    void* stream) {
   sa::Shape s;
   const sa_status st = check_desc(desc, &s);
   if (st != SA_OK) return st;
+  const bool f32_tail = desc->approx && desc->dtype == SA_DTYPE_F32;
+  const bool bf16_tail = desc->approx && desc->dtype == SA_DTYPE_BF16;
   if (!q || !k || !v || !blk_idx || !blk_cnt || !out) return SA_ERR_NULL;
-  if (desc->approx && (!k_bar || !v_sum)) return SA_ERR_NULL;
+  if (f32_tail && (!k_bar || !v_sum)) return SA_ERR_NULL;
+  if (bf16_tail && !tail) return SA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(blk_idx) ||
       !aligned16(blk_cnt))
     return SA_ERR_ALIGN;
-  if (desc->approx && (!aligned16(k_bar) || !aligned16(v_sum))) return SA_ERR_ALIGN;
+  if (f32_tail && (!aligned16(k_bar) || !aligned16(v_sum))) return SA_ERR_ALIGN;
+  if (bf16_tail && !aligned16(tail)) return SA_ERR_ALIGN;
   sa::FwdParams p;
   p.scale = resolve_scale(desc);
   p.causal = desc->causal;
   p.approx = desc->approx;
-  return from_hip(sa::launch_fwd(s, p, q, k, v, desc->approx ? k_bar : nullptr,
-                                 desc->approx ? v_sum : nullptr, blk_idx, blk_cnt, out,
+  return from_hip(sa::launch_fwd(s, p, q, k, v, f32_tail ? k_bar : nullptr, f32_tail ? v_sum : nullptr,
+                                 bf16_tail ? tail : nullptr, blk_idx, blk_cnt, out,
                                  (hipStream_t)stream));
 }

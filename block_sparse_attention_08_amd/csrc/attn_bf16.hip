@@ -9,7 +9,8 @@
 //   tail        -- with approx=1 every eligible unlisted block J is one
 //                  pseudo-key kbar_J with weight n_J in the normaliser and the
 //                  value sum SigmaV_J in the numerator (PISA explainer,
-//                  routing table and "why softmax survives");
+//                  routing table and "why softmax survives"), evaluated as
+//                  logit + ln n_J with value SigmaV_J / n_J;
 //   both are folded into one running max / sum (FlashAttention tutorial,
 //   section 2, online softmax), answer o / l.
 //
@@ -38,8 +39,9 @@
 // tile e+1 sits next to the softmax of tile e, one barrier per tile.
 // 64-row blocks keep one K and one V buffer (four workgroups per CU): the
 // next K tile loads during this tile's softmax and PV, the next V tile
-// during the next S (two barriers per tile).  Tail tiles come from the
-// float32 pooled K-bar / V-sum and are converted through registers.
+// during the next S (two barriers per tile).  Tail tiles take the same path:
+// KT pooled rows of the bf16 block means of k and v that the pool pass
+// wrote once per head.
 // Workgroups are ordered so that each XCD receives a contiguous range of
 // (kv head, query block) items, with the query heads of one KV group
 // adjacent, so K/V blocks shared by neighbouring items stay in one L2.
@@ -68,8 +70,8 @@ struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  const float* k_bar;
-  const float* v_sum;
+  const uint16_t* tail_k;   // [B, Hkv, M, D] bf16 block means of k
+  const uint16_t* tail_v;   // [B, Hkv, M, D] bf16 block means of v
   const int32_t* idx;
   const int32_t* cnt;
   uint16_t* out;
@@ -105,6 +107,17 @@ __device__ __forceinline__ int v_chunk(int r, int c) {
 }
 
 constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+
+// Combine a value of lane l with lane l ^ 32 (the two halves of a wave hold
+// the two halves of a query row): one v_permlane32_swap, no LDS traffic.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
@@ -155,35 +168,6 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int tile_off
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (i * C::NW + w) * 1024), 16,
                                              lane_off[i % DmaCfg<D, BLK>::NVAR],
                                              tile_off + i * C::NW * 1024, 0, 0);
-}
-
-// Tail tile: float32 pooled rows -> bf16 -> the same swizzled LDS layout.
-// For V the rows are divided by n_J (the block's token count: `block`, or
-// `last_n` for pooled row M-1), turning value sums into mean values; the
-// factor n_J moves into the logit instead (see mask_tail).
-template <int D, int BLK, bool IS_V>
-__device__ __forceinline__ void reg_tile(const float* src, char* lds, int valid, int w, int lane,
-                                         int last_row, float inv_last) {
-  using C = Cfg<D, BLK>;
-#pragma unroll 1
-  for (int i = 0; i < C::NI; ++i) {
-    const int P = (i * C::NW + w) * 64 + lane;
-    const int r = P / C::CPR;
-    const int pc = P % C::CPR;
-    const int c = IS_V ? v_chunk<D>(r, pc) : k_chunk<D>(r, pc);
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (r < valid) {
-      f32x4 lo = *reinterpret_cast<const f32x4*>(src + (size_t)r * D + 8 * c);
-      f32x4 hi = *reinterpret_cast<const f32x4*>(src + (size_t)r * D + 8 * c + 4);
-      if constexpr (IS_V) {
-        const float f = r == last_row ? inv_last : 1.0f / (float)BLK;
-        lo *= f;
-        hi *= f;
-      }
-      x = u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]), pack2(hi[2], hi[3])};
-    }
-    *reinterpret_cast<u32x4*>(lds + P * 16) = x;
-  }
 }
 
 template <int D, int BLK>
@@ -255,7 +239,7 @@ __device__ __forceinline__ float softmax_max(State<D, BLK>& st, const f32x16 (&s
   for (int js = 0; js < 2; ++js)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[js][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = half_max(mx);
   const float mxs = mx * c;
   const bool grow = mxs > st.m + 8.f;
   if (__ballot(grow)) {
@@ -469,6 +453,8 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k + (size_t)(b * a.Hkv + g) * a.N * D, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = head_rsrc(a.v + (size_t)(b * a.Hkv + g) * a.N * D, head_bytes);
   const size_t pp_off = (size_t)(b * a.Hkv + g) * a.M * D;
+  const __amdgpu_buffer_rsrc_t tkrs = head_rsrc(a.approx ? a.tail_k + pp_off : a.k, a.M * C::ROWB);
+  const __amdgpu_buffer_rsrc_t tvrs = head_rsrc(a.approx ? a.tail_v + pp_off : a.v, a.M * C::ROWB);
 
   // LDS byte offsets of this lane's K operand rows (per 16-wide d step) and
   // V transpose-read bases (per 32-wide d tile); tile-invariant.
@@ -497,20 +483,13 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
     koff[i] = dma_lane_off<D, BLK, false>(i, w, lane);
     voff[i] = dma_lane_off<D, BLK, true>(i, w, lane);
   }
+  // exact tiles: KT keys of the head; tail tiles: KT pooled rows (bf16 block
+  // means of k and of v from the pool pass), both straight into LDS
   auto issue_k = [&](int e, int key0) {
-    char* buf = Ks[e % NBUF];
-    if (e < n_exact)
-      dma_tile<D, BLK>(krs, key0 * C::ROWB, buf, w, koff);
-    else
-      reg_tile<D, BLK, false>(a.k_bar + pp_off + (size_t)key0 * D, buf, a.M - key0, w, lane, 0, 0.f);
+    dma_tile<D, BLK>(e < n_exact ? krs : tkrs, key0 * C::ROWB, Ks[e % NBUF], w, koff);
   };
   auto issue_v = [&](int e, int key0) {
-    char* buf = Vs[e % NBUF];
-    if (e < n_exact)
-      dma_tile<D, BLK>(vrs, key0 * C::ROWB, buf, w, voff);
-    else
-      reg_tile<D, BLK, true>(a.v_sum + pp_off + (size_t)key0 * D, buf, a.M - key0, w, lane,
-                             a.M - 1 - key0, 1.0f / (float)last_n);
+    dma_tile<D, BLK>(e < n_exact ? vrs : tvrs, key0 * C::ROWB, Vs[e % NBUF], w, voff);
   };
 
   State<D, BLK> st;
@@ -594,7 +573,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
 
   // ---- epilogue: O / l, bf16, row q_tok; register r of d-tile nt holds
   // d = 32*nt + 8*(r/4) + 4*hh + (r%4).
-  const float lt = st.l + __shfl_xor(st.l, 32, 64);
+  const float lt = half_sum(st.l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (q_ok) {
     uint16_t* orow = a.out + ((size_t)bh * a.N + q_tok) * D;
@@ -621,7 +600,7 @@ hipError_t run(const FwdArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_fwd(const Shape& s, const FwdParams& p, const void* q, const void* k,
-                      const void* v, const float* k_bar, const float* v_sum,
+                      const void* v, const float* k_bar, const float* v_sum, const void* tail,
                       const int32_t* blk_idx, const int32_t* blk_cnt, void* out, hipStream_t st) {
   if (s.dtype == 0)
     return launch_fwd_f32(s, p, q, k, v, k_bar, v_sum, blk_idx, blk_cnt, out, st);
@@ -629,8 +608,10 @@ hipError_t launch_fwd(const Shape& s, const FwdParams& p, const void* q, const v
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
-  a.k_bar = k_bar;
-  a.v_sum = v_sum;
+  if (p.approx) {
+    a.tail_k = static_cast<const uint16_t*>(tail);
+    a.tail_v = a.tail_k + (size_t)s.B * s.Hkv * s.M * s.D;
+  }
   a.idx = blk_idx;
   a.cnt = blk_cnt;
   a.out = static_cast<uint16_t*>(out);

@@ -12,9 +12,10 @@ struct Shape {
   int dtype;  // 0 = f32, 1 = bf16
 };
 
-// Stage 1: block means of q and k, block sums of v (v may be null).
+// Stage 1: block means of q and k, block sums of v (v may be null); with a
+// non-null `tail` also the bf16 block means of k and of v (2 x [B,Hkv,M,D]).
 hipError_t launch_pool(const Shape& s, const void* q, const void* k, const void* v,
-                       float* q_bar, float* k_bar, float* v_sum, hipStream_t st);
+                       float* q_bar, float* k_bar, float* v_sum, void* tail, hipStream_t st);
 
 // Stage 2: pooled scores + selection + compaction.
 struct SelectParams {
@@ -35,7 +36,7 @@ struct FwdParams {
   int approx;
 };
 hipError_t launch_fwd(const Shape& s, const FwdParams& p, const void* q, const void* k,
-                      const void* v, const float* k_bar, const float* v_sum,
+                      const void* v, const float* k_bar, const float* v_sum, const void* tail,
                       const int32_t* blk_idx, const int32_t* blk_cnt, void* out, hipStream_t st);
 
 // Largest number of key blocks per row the selection kernel supports.

@@ -19,6 +19,7 @@ namespace {
 struct PoolArgs {
   const void* src[3];
   float* dst[3];
+  uint16_t* tail[3];  // bf16 copies: [1] block means of k, [2] block means of v
   int items[3];   // B * heads * M for q, k, v (v: 0 when not pooled)
   int is_mean[3];
   int N, M, block;
@@ -85,6 +86,10 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     for (int r = 0; r < RPP; ++r) s += red[r][t];
     if (a.is_mean[which]) s = s / (float)n;
     a.dst[which][(size_t)item * D + t] = s;
+    // bf16 tail operands: the pseudo-key (mean k) and its value (mean v)
+    if (a.tail[which])
+      a.tail[which][(size_t)item * D + t] =
+          (uint16_t)f32_to_bf16_bits(a.is_mean[which] ? s : s / (float)n);
   }
 }
 
@@ -97,7 +102,7 @@ hipError_t run(const PoolArgs& a, int grid, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_pool(const Shape& s, const void* q, const void* k, const void* v,
-                       float* q_bar, float* k_bar, float* v_sum, hipStream_t st) {
+                       float* q_bar, float* k_bar, float* v_sum, void* tail, hipStream_t st) {
   PoolArgs a{};
   a.src[0] = q;
   a.src[1] = k;
@@ -108,6 +113,10 @@ hipError_t launch_pool(const Shape& s, const void* q, const void* k, const void*
   a.items[0] = s.B * s.Hq * s.M;
   a.items[1] = s.B * s.Hkv * s.M;
   a.items[2] = (v && v_sum) ? s.B * s.Hkv * s.M : 0;
+  if (tail && v && v_sum) {
+    a.tail[1] = static_cast<uint16_t*>(tail);
+    a.tail[2] = static_cast<uint16_t*>(tail) + (size_t)s.B * s.Hkv * s.M * s.D;
+  }
   a.is_mean[0] = 1;
   a.is_mean[1] = 1;
   a.is_mean[2] = 0;

@@ -54,6 +54,10 @@
  *   q_bar [batch, heads_q,  M, head_dim] float32  (block means of q)
  *   k_bar [batch, heads_kv, M, head_dim] float32  (block means of k)
  *   v_sum [batch, heads_kv, M, head_dim] float32  (block sums of v)
+ *   tail  bf16 inputs with approx=1 only: [2, batch, heads_kv, M, head_dim]
+ *         bfloat16 -- the block means of k, then the block means of v
+ *         (v_sum / n_J): the pseudo-keys and their values in the matrix-core
+ *         dtype, written once by the pool pass for all query blocks
  *   blk_idx [batch, heads_q, M, M] int32: row (b,h,I) holds blk_cnt[b,h,I]
  *           strictly ascending eligible key-block indices; entries past the
  *           count are unspecified (sparse_attn_select uses the whole buffer
@@ -87,7 +91,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 1
+#define SPARSE_ATTN_ABI_VERSION 2
 
 typedef enum {
   SA_OK = 0,
@@ -120,20 +124,22 @@ typedef struct {
 } sa_desc;
 
 typedef struct {        /* bytes of each caller-allocated buffer */
-  size_t q_bar, k_bar, v_sum, blk_idx, blk_cnt;
+  size_t q_bar, k_bar, v_sum, tail, blk_idx, blk_cnt;
 } sa_sizes;
 
 /* Bytes needed for the intermediate buffers of `desc` (host only, no GPU).
- * v_sum is 0 when approx == 0.  Errors: SA_ERR_NULL, SA_ERR_SHAPE,
- * SA_ERR_DTYPE, SA_ERR_PARAM, SA_ERR_UNSUPPORTED. */
+ * v_sum is 0 when approx == 0; tail is 0 unless approx == 1 and dtype is
+ * bf16.  Errors: SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_DTYPE, SA_ERR_PARAM,
+ * SA_ERR_UNSUPPORTED. */
 sa_status sparse_attn_buffer_sizes(const sa_desc* desc, sa_sizes* sizes);
 
 /* Stage 1, block pooling: one pass over q, k (and v when approx) writing
- * q_bar, k_bar (block means) and v_sum (block sums), float32.  v and v_sum
- * may be NULL when approx == 0 (then they are ignored). */
+ * q_bar, k_bar (block means) and v_sum (block sums), float32, and for bf16
+ * inputs with approx the bf16 tail operands.  v, v_sum and tail may be NULL
+ * when approx == 0 (then they are ignored); tail may be NULL for float32. */
 sa_status sparse_attn_block_pool(const sa_desc* desc, const void* q, const void* k,
                                  const void* v, float* q_bar, float* k_bar, float* v_sum,
-                                 void* stream);
+                                 void* tail, void* stream);
 
 /* Stage 2, scoring + selection: pooled scores (float32, held in blk_idx as
  * scratch), alpha-threshold or top-k selection, compaction of every row in
@@ -143,12 +149,14 @@ sa_status sparse_attn_select(const sa_desc* desc, const float* q_bar, const floa
 
 /* Stage 3, attention: exact online-softmax attention over the listed blocks
  * (+ the 0th-order tail over unlisted eligible blocks when approx == 1),
- * output in dtype.  k_bar / v_sum may be NULL when approx == 0.  The lists
- * may come from sparse_attn_select or from the caller (e.g. every eligible
- * block for dense attention). */
+ * output in dtype.  The tail reads k_bar / v_sum for float32 inputs and
+ * `tail` for bf16 inputs; unused ones may be NULL (all three when
+ * approx == 0).  The lists may come from sparse_attn_select or from the
+ * caller (e.g. every eligible block for dense attention). */
 sa_status sparse_attn_fwd(const sa_desc* desc, const void* q, const void* k, const void* v,
-                          const float* k_bar, const float* v_sum, const int32_t* blk_idx,
-                          const int32_t* blk_cnt, void* out, void* stream);
+                          const float* k_bar, const float* v_sum, const void* tail,
+                          const int32_t* blk_idx, const int32_t* blk_cnt, void* out,
+                          void* stream);
 
 /* Static, human-readable text of a status code. */
 const char* sparse_attn_status_string(sa_status status);

@@ -60,7 +60,7 @@ def run_gpu(q, k, v, *, dtype, block, causal, approx, mode, alpha=0.5, density=0
     qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
     ws = bsa.Workspace(desc)
     out = torch.empty_like(qd)
-    bsa.block_pool(desc, qd, kd, vd, ws.q_bar, ws.k_bar, ws.v_sum)
+    bsa.block_pool(desc, qd, kd, vd, ws.q_bar, ws.k_bar, ws.v_sum, ws.tail)
     bsa.select(desc, ws.q_bar, ws.k_bar, ws.blk_idx, ws.blk_cnt)
     if sel_mask is not None:
         idx, cnt = oracle.mask_to_lists(sel_mask)
@@ -68,7 +68,7 @@ def run_gpu(q, k, v, *, dtype, block, causal, approx, mode, alpha=0.5, density=0
         fcnt = torch.from_numpy(cnt).cuda()
     else:
         fidx, fcnt = ws.blk_idx, ws.blk_cnt
-    bsa.fwd(desc, qd, kd, vd, ws.k_bar, ws.v_sum, fidx, fcnt, out)
+    bsa.fwd(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, fidx, fcnt, out)
     torch.cuda.synchronize()
     res = dict(q_bar=to_host(ws.q_bar), k_bar=to_host(ws.k_bar),
                v_sum=None if ws.v_sum is None else to_host(ws.v_sum),

@@ -34,7 +34,7 @@ def test_struct_layout_matches_header():
     # int32 x8, double x2, float, int32 x2 -> 64 bytes with natural alignment
     assert ctypes.sizeof(_lib.SaDesc) == 64
     assert _lib.SaDesc.alpha.offset == 32 and _lib.SaDesc.scale.offset == 48
-    assert ctypes.sizeof(_lib.SaSizes) == 5 * ctypes.sizeof(ctypes.c_size_t)
+    assert ctypes.sizeof(_lib.SaSizes) == 6 * ctypes.sizeof(ctypes.c_size_t)
 
 
 @needs_lib
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
     h = _lib.lib()
     for name in _declared():
         assert hasattr(h, name), name
-    assert bsa.abi_version() == 1
+    assert bsa.abi_version() == 2
 
 
 @needs_lib
@@ -69,10 +69,12 @@ def test_buffer_sizes_image_workload():
     assert s["q_bar"] == 24 * M * 128 * 4
     assert s["k_bar"] == 24 * M * 128 * 4
     assert s["v_sum"] == 24 * M * 128 * 4
+    assert s["tail"] == 2 * 24 * M * 128 * 2
     assert s["blk_idx"] == 24 * M * M * 4
     assert s["blk_cnt"] == 24 * M * 4
     s0 = bsa.buffer_sizes(_desc(approx=False, N=32760))
-    assert s0["v_sum"] == 0 and s0["blk_cnt"] == 24 * 512 * 4
+    assert s0["v_sum"] == 0 and s0["tail"] == 0 and s0["blk_cnt"] == 24 * 512 * 4
+    assert bsa.buffer_sizes(_desc(dtype="f32", d=64))["tail"] == 0
 
 
 @needs_lib
@@ -82,6 +84,7 @@ def test_buffer_sizes_image_workload():
     (dict(d=96), 6),
     (dict(block=32), 6),
     (dict(N=2049 * 64), 6),          # more than 2048 blocks
+    (dict(B=2, Hq=40000, Hkv=40000), 6),   # batch * heads beyond the score grid
     (dict(density=1.5), 4),
     (dict(density=0.0), 4),
     (dict(density=None, alpha=0.0), 4),
@@ -116,9 +119,9 @@ def test_bad_dtype_and_flags():
 def test_compute_calls_reject_null_pointers_before_launch():
     h = _lib.lib()
     d = _desc()
-    assert h.sparse_attn_block_pool(d, None, None, None, None, None, None, None) == 1
+    assert h.sparse_attn_block_pool(d, None, None, None, None, None, None, None, None) == 1
     assert h.sparse_attn_select(d, None, None, None, None, None) == 1
-    assert h.sparse_attn_fwd(d, None, None, None, None, None, None, None, None, None) == 1
+    assert h.sparse_attn_fwd(d, None, None, None, None, None, None, None, None, None, None) == 1
     assert h.sparse_attn_buffer_sizes(None, None) == 1
     # misaligned (never dereferenced: validation returns first)
     bad = ctypes.c_void_p(0x1003)

@@ -137,7 +137,7 @@ def test_caller_lists_dense_causal():
     cnt = np.broadcast_to(np.arange(1, M + 1, dtype=np.int32), (1, 4, M)).copy()
     qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
     out = torch.empty_like(qd)
-    bsa.fwd(desc, qd, kd, vd, None, None, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), out)
+    bsa.fwd(desc, qd, kd, vd, None, None, None, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), out)
     ref = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(q).double(), torch.from_numpy(k).double().repeat_interleave(2, 1),
         torch.from_numpy(v).double().repeat_interleave(2, 1), is_causal=True).numpy()
