@@ -226,6 +226,8 @@ def main():
     elt = 2 if wl.dtype == "bf16" else 4
     n_pool_heads = wl.Hq + wl.Hkv * (2 if wl.approx else 1)
     pool_bytes = wl.B * n_pool_heads * (wl.N * wl.d * elt + M * wl.d * 4)
+    if wl.approx and wl.dtype == "bf16":
+        pool_bytes += 2 * wl.B * wl.Hkv * M * wl.d * 2      # bf16 tail operands
     n_elig = wl.B * wl.Hq * (M * (M + 1) // 2 if wl.causal else M * M)
     sel_flops = 2.0 * wl.d * n_elig
     sel_bytes = wl.B * (wl.Hq + wl.Hkv) * M * wl.d * 4 + 4 * (int(cnt_h.sum()) + cnt_h.size)

@@ -133,3 +133,14 @@ def test_make_desc_needs_exactly_one_rule():
         bsa.make_desc(1, 1, 1, 64, 64, block=64, dtype="bf16")
     with pytest.raises(ValueError):
         bsa.make_desc(1, 1, 1, 64, 64, block=64, dtype="bf16", alpha=0.5, density=0.1)
+
+
+@needs_lib
+def test_one_hip_runtime_in_process():
+    """The library binds to the HIP runtime torch already loaded (one runtime,
+    so torch's streams and device pointers are valid inside the library)."""
+    import torch  # noqa: F401
+    _lib.lib()
+    maps = open("/proc/self/maps").read()
+    runtimes = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(runtimes) == 1, runtimes
