@@ -47,6 +47,7 @@
 // adjacent, so K/V blocks shared by neighbouring items stay in one L2.
 #include <math.h>
 
+#include "attn_common.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -56,15 +57,11 @@ hipError_t launch_fwd_f32(const Shape& s, const FwdParams& p, const void* q, con
                           const void* v, const float* k_bar, const float* v_sum,
                           const int32_t* blk_idx, const int32_t* blk_cnt, void* out,
                           hipStream_t st);
+hipError_t launch_fwd_w16(const Shape& s, const FwdParams& p, const void* q, const void* k,
+                          const void* v, const void* tail, const int32_t* blk_idx,
+                          const int32_t* blk_cnt, void* out, hipStream_t st);
 
 namespace {
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct FwdArgs {
   const uint16_t* q;
@@ -79,8 +76,6 @@ struct FwdArgs {
   float scale_log2;  // scale * log2(e)
   int causal, approx;
 };
-
-constexpr int KT = 64;  // keys per tile (a 128-token block is two tiles)
 
 template <int D, int BLK>
 struct Cfg {
@@ -106,8 +101,6 @@ __device__ __forceinline__ int v_chunk(int r, int c) {
   return D == 128 ? c ^ (((r & 3) << 2) | (r & 2)) : c ^ ((r & 3) << 1);
 }
 
-constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
-
 // Combine a value of lane l with lane l ^ 32 (the two halves of a wave hold
 // the two halves of a query row): one v_permlane32_swap, no LDS traffic.
 __device__ __forceinline__ float half_max(float x) {
@@ -119,13 +112,7 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
 
-// Wait until this wave's outstanding global loads (including the ones that
-// write LDS directly) have completed.
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Byte offset, inside a KT x D tile, of the global 16-byte chunk this lane
 // copies with direct load i: instruction i of wave w fills LDS chunks
@@ -150,12 +137,6 @@ __device__ __forceinline__ int dma_lane_off(int i, int w, int lane) {
   return (r - i * C::NW * DmaCfg<D, BLK>::ROWS_PER_KB) * C::ROWB + c * 16;
 }
 
-// Buffer resource over one K or V head ([N, D] bf16): loads past its last
-// byte return zero, which is what the rows of a ragged last block need
-// (their keys are masked and their values meet p = 0).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
-}
 
 // Direct HBM -> LDS load of one exact K or V tile: KT rows starting at byte
 // `tile_off` of the head.
@@ -604,6 +585,8 @@ hipError_t launch_fwd(const Shape& s, const FwdParams& p, const void* q, const v
                       const int32_t* blk_idx, const int32_t* blk_cnt, void* out, hipStream_t st) {
   if (s.dtype == 0)
     return launch_fwd_f32(s, p, q, k, v, k_bar, v_sum, blk_idx, blk_cnt, out, st);
+  // 64-row query blocks: 16 rows per wave (four waves share one K/V tile)
+  if (s.block == 64) return launch_fwd_w16(s, p, q, k, v, tail, blk_idx, blk_cnt, out, st);
   FwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);

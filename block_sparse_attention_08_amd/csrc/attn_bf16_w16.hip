@@ -1,0 +1,382 @@
+// Stage 3 for bf16 inputs, 16 query rows per wave: block-sparse flash
+// attention on the gfx950 matrix cores with v_mfma_f32_16x16x32_bf16.
+//
+// Computes exactly what attn_bf16.hip computes (exact softmax over the
+// listed key blocks, FlashPrefill summary 2(c) index-driven tiles; the
+// 0th-order tail of unlisted eligible blocks as pseudo-keys with weight n_J,
+// PISA explainer routing table; one running max / sum, FlashAttention
+// tutorial section 2).  The difference is the work split: a workgroup of
+// block/16 waves, each owning 16 query rows, so one K tile and one V tile in
+// LDS (32 KB) feed four waves of a 64-row block -- four workgroups, sixteen
+// waves per CU -- where the 32-row layout fits only eight.
+//
+// Per 64-key tile and wave:
+//   S^T = K Q^T: 4 key groups x d/32 steps of 16x16x32 (K from LDS as A,
+//       the wave's Q rows in registers as B).  Lane l holds query row l%16,
+//       keys 16t + 4*(l/16) + r of key group t: a row's 64 scores sit in
+//       the four lanes l%16 + 16g, combined with two permlane swaps.
+//   P = exp2(S * scale * log2 e - m), packed to bf16: the registers of key
+//       groups 2c and 2c+1 are directly the B operand of PV step c.
+//   O^T += V^T P^T: d/16 tiles x 2 steps; V^T gathered from the row-major V
+//       tile with ds_read_b64_tr_b16.
+// K/V tiles move HBM -> LDS with buffer loads straight into LDS (range-
+// checked: rows past the last key read zero), XOR-swizzled per row (K:
+// chunk ^ (row & 15), V: chunk ^ 2*(row & 7) for d = 128) so the operand
+// reads are free of bank conflicts.  One K and one V buffer, two barriers per
+// tile: the next K tile loads during softmax and PV, the next V tile during
+// the next S.
+#include <math.h>
+
+#include "attn_common.h"
+#include "device_common.h"
+#include "launch.h"
+
+namespace sa {
+namespace {
+
+struct Args {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* tail_k;
+  const uint16_t* tail_v;
+  const int32_t* idx;
+  const int32_t* cnt;
+  uint16_t* out;
+  int Hq, Hkv, N, M, G, total;
+  float scale_log2;
+  int causal, approx;
+};
+
+template <int D, int BLK>
+struct Cfg {
+  static constexpr int NW = BLK / 16;         // waves
+  static constexpr int NT = 64 * NW;          // threads
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int NI = KT * CPR / NT;    // 16-byte DMA loads per thread per tile
+  static constexpr int NKS = D / 32;          // 32-wide d steps of S
+  static constexpr int NOT = D / 16;          // 16-wide d tiles of O
+  static constexpr int ROWB = D * 2;          // bytes per LDS row
+  static constexpr int RPK = 1024 / ROWB;     // rows filled by one 1 KB DMA instruction
+  static_assert(NI >= 1 && (NW * RPK) % 16 == 0, "per-lane DMA offsets must repeat every instruction");
+};
+
+template <int D>
+__device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & (D == 128 ? 15 : 7)); }
+template <int D>
+__device__ __forceinline__ int v_chunk(int r, int c) { return c ^ (D == 128 ? 2 * (r & 7) : 2 * (r & 3)); }
+
+// Byte offset in the tile of the 16-byte chunk this lane copies with every
+// DMA instruction (instruction i adds i*NW KB: whole rows, and the swizzle
+// repeats every 16 rows).
+template <int D, int BLK, bool IS_V>
+__device__ __forceinline__ int dma_lane_off(int w, int lane) {
+  using C = Cfg<D, BLK>;
+  const int P = w * 64 + lane;
+  const int r = P / C::CPR, pc = P % C::CPR;
+  const int c = IS_V ? v_chunk<D>(r, pc) : k_chunk<D>(r, pc);
+  return r * C::ROWB + c * 16;
+}
+
+template <int D, int BLK>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int tile_off, char* lds, int w,
+                                         int lane_off) {
+  using C = Cfg<D, BLK>;
+#pragma unroll
+  for (int i = 0; i < C::NI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (i * C::NW + w) * 1024), 16, lane_off,
+                                             tile_off + i * C::NW * 1024, 0, 0);
+}
+
+// value of a query row over its four lanes (l%16 + 16g)
+__device__ __forceinline__ float row_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
+  using C = Cfg<D, BLK>;
+  __shared__ __attribute__((aligned(1024))) char Ks[KT * D * 2];
+  __shared__ __attribute__((aligned(1024))) char Vs[KT * D * 2];
+  // one spare word: the tail mask reads the word after the tile's first
+  __shared__ uint32_t selbits[kMaxBlocks / 32 + 1];
+
+  const int item = xcd_local_item(blockIdx.x, a.total);
+  if (item < 0) return;
+  const int hg = item % a.G;
+  int rest = item / a.G;
+  const int I = a.M - 1 - rest % a.M;
+  rest /= a.M;
+  const int g = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  const int h = g * a.G + hg;
+  const int bh = b * a.Hq + h;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lr = lane & 15;   // query row inside the wave
+  const int lg = lane >> 4;   // lane group: keys 4*lg .. 4*lg+3 of every key group
+
+  const int q_tok = I * BLK + 16 * w + lr;
+  const bool q_ok = q_tok < a.N;
+
+  // Q fragment (B operand of S^T): row q_tok, d = 32*s + 8*lg + e
+  bf16x8 qf[C::NKS];
+  {
+    const uint16_t* qrow = a.q + ((size_t)bh * a.N + (q_ok ? q_tok : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < C::NKS; ++s) {
+      const u32x4 x = q_ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * lg) : u32x4{0u, 0u, 0u, 0u};
+      qf[s] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  const int n_sel = a.cnt[(size_t)bh * a.M + I];
+  const int32_t* list = a.idx + ((size_t)bh * a.M + I) * a.M;
+  const int Jend = a.causal ? I + 1 : a.M;
+  constexpr int SUB = BLK / KT;
+  const int n_exact = n_sel * SUB;
+  const int n_tiles = n_exact + (a.approx ? (Jend + KT - 1) / KT : 0);
+  const int last_n = a.N - (a.M - 1) * BLK;
+  const float bias_blk = __log2f((float)BLK) / a.scale_log2;
+  const float bias_last = __log2f((float)last_n) / a.scale_log2;
+
+  if (a.approx) {
+    for (int i = t; i < kMaxBlocks / 32 + 1; i += C::NT) selbits[i] = 0u;
+    __syncthreads();
+    for (int e = t; e < n_sel; e += C::NT) {
+      const int J = list[e];
+      atomicOr(&selbits[J >> 5], 1u << (J & 31));
+    }
+  }
+
+  const int head_bytes = a.N * C::ROWB;
+  const size_t pp_off = (size_t)(b * a.Hkv + g) * a.M * D;
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k + (size_t)(b * a.Hkv + g) * a.N * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(a.v + (size_t)(b * a.Hkv + g) * a.N * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t tkrs = head_rsrc(a.approx ? a.tail_k + pp_off : a.k, a.M * C::ROWB);
+  const __amdgpu_buffer_rsrc_t tvrs = head_rsrc(a.approx ? a.tail_v + pp_off : a.v, a.M * C::ROWB);
+  const int koff = dma_lane_off<D, BLK, false>(w, lane);
+  const int voff = dma_lane_off<D, BLK, true>(w, lane);
+
+  // LDS operand addresses (tile-invariant): K rows 16t + lr, chunk 4s + lg;
+  // V transpose-read source rows 4*lg + (lr >> 2) (+32c, +16 half), columns
+  // 16nt + 4*(lr & 3)
+  int kbase[C::NKS];
+#pragma unroll
+  for (int s = 0; s < C::NKS; ++s) kbase[s] = lr * C::ROWB + k_chunk<D>(lr, 4 * s + lg) * 16;
+  int vbase[C::NOT];
+  {
+    const int jr = 4 * lg + (lr >> 2);
+#pragma unroll
+    for (int nt = 0; nt < C::NOT; ++nt) {
+      const int n = 16 * nt + 4 * (lr & 3);
+      vbase[nt] = jr * C::ROWB + v_chunk<D>(jr, n >> 3) * 16 + (n & 7) * 2;
+    }
+  }
+
+  auto tile_key0 = [&](int e) -> int {
+    if (e < n_exact) return list[e / SUB] * BLK + (e % SUB) * KT;
+    return (e - n_exact) * KT;
+  };
+  auto issue_k = [&](int e, int key0) {
+    dma_tile<D, BLK>(e < n_exact ? krs : tkrs, key0 * C::ROWB, Ks, w, koff);
+  };
+  auto issue_v = [&](int e, int key0) {
+    dma_tile<D, BLK>(e < n_exact ? vrs : tvrs, key0 * C::ROWB, Vs, w, voff);
+  };
+
+  f32x4 o[C::NOT];
+#pragma unroll
+  for (int i = 0; i < C::NOT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;   // running reference max (scaled log2 domain)
+  float l = 0.f;         // this lane's partial row sum
+  const float c = a.scale_log2;
+
+  int key0 = tile_key0(0);
+  issue_k(0, key0);
+  issue_v(0, key0);
+  wait_vm();
+  __syncthreads();
+
+  for (int e = 0; e < n_tiles; ++e) {
+    const int key1 = e + 1 < n_tiles ? tile_key0(e + 1) : 0;
+
+    // ---- S^T = K Q^T (K operands read three steps ahead)
+    f32x4 s[4];
+    {
+      constexpr int NSTEP = 4 * C::NKS;
+      constexpr int KD = 3;
+      bf16x8 kr[KD];
+#pragma unroll
+      for (int i = 0; i < KD; ++i)
+        kr[i] = *reinterpret_cast<const bf16x8*>(Ks + kbase[i % C::NKS] + 16 * (i / C::NKS) * C::ROWB);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int step = 0; step < NSTEP; ++step) {
+        const int tg = step / C::NKS, ks = step % C::NKS;
+        const bf16x8 ka = kr[step % KD];
+        if (step + KD < NSTEP) {
+          const int n2 = step + KD;
+          kr[step % KD] = *reinterpret_cast<const bf16x8*>(Ks + kbase[n2 % C::NKS] + 16 * (n2 / C::NKS) * C::ROWB);
+        }
+        s[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], s[tg], 0, 0, 0);
+      }
+    }
+    wait_vm();
+    __syncthreads();                 // K buffer free, V tile e landed in every wave
+    if (e + 1 < n_tiles) issue_k(e + 1, key1);
+
+    // ---- masks: register r of key group tg holds key key0 + 16*tg + 4*lg + r
+    if (e >= n_exact) {
+      const int lim = Jend - key0 - 4 * lg;
+      const int last_kr = a.M - 1 - key0 - 4 * lg;
+      const uint32_t w0 = selbits[key0 >> 5] >> (4 * lg);
+      const uint32_t w1 = selbits[(key0 >> 5) + 1] >> (4 * lg);
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg) {
+        const uint32_t word = tg < 2 ? w0 : w1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kr = 16 * tg + r;            // key - key0 - 4*lg
+          const bool on = kr < lim && !((word >> (kr & 31)) & 1u);
+          s[tg][r] = on ? s[tg][r] + (kr == last_kr ? bias_last : bias_blk) : -INFINITY;
+        }
+      }
+    } else if (key0 + KT > a.N || (a.causal && key0 + KT > I * BLK)) {
+      int lim = a.N - key0;
+      if (a.causal) lim = min(lim, q_tok - key0 + 1);
+      lim -= 4 * lg;
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[tg][r] = 16 * tg + r < lim ? s[tg][r] : -INFINITY;
+    }
+
+    // ---- online softmax
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[tg][r]);
+    mx = row_max4(mx);
+    const float mxs = mx * c;
+    const bool grow = mxs > m + 8.f;
+    if (__ballot(grow)) {
+      const float m_new = grow ? mxs : m;
+      const float corr = __builtin_amdgcn_exp2f(m - m_new);
+      l *= corr;
+#pragma unroll
+      for (int nt = 0; nt < C::NOT; ++nt) o[nt] *= corr;
+      m = m_new;
+    }
+    const float mb = m == -INFINITY ? 0.f : m;
+    uint32_t wd[8];
+    float lsum = 0.f;
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+#pragma unroll
+      for (int hp = 0; hp < 2; ++hp) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[tg][2 * hp], c, -mb));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[tg][2 * hp + 1], c, -mb));
+        wd[2 * tg + hp] = pack2(p0, p1);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[2 * tg + hp]), kOnes, lsum, false);
+      }
+    }
+    l += lsum;
+    // PV step cc (keys 32cc .. 32cc+31): slots 0-3 = key group 2cc, 4-7 = 2cc+1
+    bf16x8 pk[2];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+      pk[cc] = __builtin_bit_cast(bf16x8, u32x4{wd[4 * cc], wd[4 * cc + 1], wd[4 * cc + 2], wd[4 * cc + 3]});
+
+    // ---- O^T += V^T P^T (V operands four ahead)
+    {
+      constexpr int NPV = 2 * C::NOT;
+      constexpr int VD = 4;
+      auto vop = [&](int j) -> bf16x8 {
+        const int nt = j >> 1, cc = j & 1;
+        const char* p = Vs + vbase[nt] + (32 * cc) * C::ROWB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * C::ROWB));
+        return __builtin_bit_cast(
+            bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      };
+      bf16x8 vr[VD];
+#pragma unroll
+      for (int j = 0; j < VD; ++j) vr[j] = vop(j);
+#pragma unroll
+      for (int j = 0; j < NPV; ++j) {
+        const bf16x8 va = vr[j % VD];
+        if (j + VD < NPV) vr[j % VD] = vop(j + VD);
+        o[j >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[j & 1], o[j >> 1], 0, 0, 0);
+      }
+    }
+
+    wait_vm();
+    __syncthreads();                 // V buffer free, K tile e+1 landed in every wave
+    if (e + 1 < n_tiles) issue_v(e + 1, key1);
+    key0 = key1;
+  }
+
+  // ---- epilogue: register r of d-tile nt holds d = 16*nt + 4*lg + r
+  const float lt = row_sum4(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (q_ok) {
+    uint16_t* orow = a.out + ((size_t)bh * a.N + q_tok) * D;
+#pragma unroll
+    for (int nt = 0; nt < C::NOT; ++nt) {
+      const u32x2 x = {pack2(o[nt][0] * inv, o[nt][1] * inv), pack2(o[nt][2] * inv, o[nt][3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + 16 * nt + 4 * lg) = x;
+    }
+  }
+}
+
+template <int D, int BLK>
+hipError_t run(const Args& a, hipStream_t st) {
+  const int grid = 8 * ((a.total + 7) / 8);
+  hipLaunchKernelGGL((attn_w16_kernel<D, BLK>), dim3(grid), dim3(4 * BLK), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_w16(const Shape& s, const FwdParams& p, const void* q, const void* k,
+                          const void* v, const void* tail, const int32_t* blk_idx,
+                          const int32_t* blk_cnt, void* out, hipStream_t st) {
+  Args a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  if (p.approx) {
+    a.tail_k = static_cast<const uint16_t*>(tail);
+    a.tail_v = a.tail_k + (size_t)s.B * s.Hkv * s.M * s.D;
+  }
+  a.idx = blk_idx;
+  a.cnt = blk_cnt;
+  a.out = static_cast<uint16_t*>(out);
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.N = s.N;
+  a.M = s.M;
+  a.G = s.Hq / s.Hkv;
+  a.total = s.B * s.Hq * s.M;
+  a.scale_log2 = p.scale * 1.4426950408889634f;
+  a.causal = p.causal;
+  a.approx = p.approx;
+  if (s.D == 128) return s.block == 128 ? run<128, 128>(a, st) : run<128, 64>(a, st);
+  return s.block == 128 ? run<64, 128>(a, st) : run<64, 64>(a, st);
+}
+
+}  // namespace sa

@@ -1,0 +1,36 @@
+// Internal helpers shared by the bf16 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace sa {
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int KT = 64;  // keys per tile (a 128-token block is two tiles)
+
+constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+
+// two floats -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// Wait until this wave's outstanding global loads (including the ones that
+// write LDS directly) have completed.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Buffer resource over one [rows, D] bf16 head of `bytes` bytes: loads past
+// the end return zero (rows of a ragged last block, pooled rows past M).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+}
+
+}  // namespace sa
