@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--workload", default="dit_image_8k")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-peaks", action="store_true",
+                   help="skip the achievable-rate kernels (streaming read, MFMA loop)")
     p.add_argument("--cpu-budget-s", type=float, default=12.0,
                    help="CPU seconds the oracle sample may take (whole heads)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -102,6 +104,40 @@ def read_traffic(workload):
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def achievable_peaks(dev, read_mib=2048, reps=5, mfma_iters=20000):
+    """Rates the machine reaches with the two measurement kernels of
+    libsa_peaks.so: a streaming read of a buffer 8x the last-level cache and a
+    loop of independent bf16 matrix-core products, timed with events on the
+    launch stream."""
+    import ctypes
+    import torch
+    from block_sparse_attention_08_amd import _lib
+    h = _lib.peaks_lib()
+    st = torch.cuda.current_stream()
+    buf = torch.zeros(read_mib << 20, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    got = ctypes.c_size_t(0)
+    flops = ctypes.c_double(0.0)
+
+    def timed(fn):
+        assert fn() == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            assert fn() == 0
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t_read = timed(lambda: h.sa_peak_read(buf.data_ptr(), buf.numel(), sink.data_ptr(),
+                                          st.cuda_stream, ctypes.byref(got)))
+    t_mfma = timed(lambda: h.sa_peak_mfma_bf16(mfma_iters, sink.data_ptr(), st.cuda_stream,
+                                               ctypes.byref(flops)))
+    del buf
+    return got.value / t_read / 1e9, flops.value / t_mfma / 1e12
 
 
 def cpu_baseline(wl, seed, budget_s):
@@ -256,7 +292,9 @@ def main():
                                  else f"density={wl.density}") if not args.dense else "all",
                    "tail": bool(wl.approx and not args.dense), "parallelism": "single-gpu"},
         "roofline": {
-            "bound": "mfma", "kernel": "attn_bf16_kernel" if wl.dtype == "bf16" else "attn_f32_kernel",
+            "bound": "mfma",
+            "kernel": ("attn_f32_kernel" if wl.dtype != "bf16" else
+                       "attn_w16_kernel" if wl.block == 64 else "attn_bf16_kernel"),
             "achieved": round(eff_tflops_fwd, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(eff_tflops_fwd / peak, 4),
             "traffic": traffic,
@@ -266,6 +304,7 @@ def main():
             "pool_GBps": round(pool_bytes / (ms_pool * 1e-3) / 1e9, 1),
             "pool_hbm_frac": round(pool_bytes / (ms_pool * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "select_TFLOPs": round(sel_flops / (ms_sel * 1e-3) / 1e12, 2),
+            "select_hbm_frac": round(sel_bytes / (ms_sel * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "pool_select_hbm_frac": round((pool_bytes + sel_bytes) / ((ms_pool + ms_sel) * 1e-3)
                                           / 1e9 / PEAK_HBM_GBS, 4),
             "exact_pairs": int(ex), "tail_pairs": int(tl), "algorithmic_gflop": round(flops / 1e9, 3),
@@ -275,6 +314,18 @@ def main():
                                         * (0.5 if wl.causal else 1.0) / (ms_step * 1e-3) / 1e12, 2),
         },
     }
+    if not args.no_peaks:
+        print("[bench] measuring achievable HBM read and bf16 MFMA rates", file=sys.stderr, flush=True)
+        hbm, mfma = achievable_peaks(dev)
+        pool_gbps = pool_bytes / (ms_pool * 1e-3) / 1e9
+        result["achievable"] = {
+            "hbm_read_GBps": round(hbm, 1), "mfma_bf16_TFLOPs": round(mfma, 1),
+            "pool_frac_of_achievable_hbm": round(pool_gbps / hbm, 4),
+            "pool_select_frac_of_achievable_hbm": round(
+                (pool_bytes + sel_bytes) / ((ms_pool + ms_sel) * 1e-3) / 1e9 / hbm, 4),
+            "fwd_frac_of_achievable_mfma": (round(eff_tflops_fwd / mfma, 4)
+                                            if wl.dtype == "bf16" else None),
+        }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, args.seed, args.cpu_budget_s)

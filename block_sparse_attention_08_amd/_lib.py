@@ -13,6 +13,7 @@ import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "lib", "libsparse_attn.so")
+PEAKS_PATH = os.path.join(PKG, "lib", "libsa_peaks.so")
 
 SA_DTYPE_F32, SA_DTYPE_BF16 = 0, 1
 SA_SELECT_ALPHA, SA_SELECT_DENSITY = 0, 1
@@ -52,6 +53,7 @@ class SparseAttnError(ValueError):
 
 
 _lib = None
+_peaks = None
 _lock = threading.Lock()
 
 _P = ctypes.c_void_p
@@ -86,6 +88,25 @@ def lib() -> ctypes.CDLL:
             h.sparse_attn_abi_version.restype = ctypes.c_int32
             _lib = h
     return _lib
+
+
+def peaks_lib() -> ctypes.CDLL:
+    """libsa_peaks.so: the achievable-rate kernels (measurement only)."""
+    global _peaks
+    if _peaks is not None:
+        return _peaks
+    with _lock:
+        if _peaks is None:
+            if not os.path.exists(PEAKS_PATH):
+                raise RuntimeError(f"{PEAKS_PATH} is missing: build the HIP libraries first")
+            import torch  # noqa: F401
+            h = ctypes.CDLL(PEAKS_PATH)
+            h.sa_peak_read.argtypes = [_P, ctypes.c_size_t, _P, _P, ctypes.POINTER(ctypes.c_size_t)]
+            h.sa_peak_read.restype = ctypes.c_int
+            h.sa_peak_mfma_bf16.argtypes = [ctypes.c_int, _P, _P, ctypes.POINTER(ctypes.c_double)]
+            h.sa_peak_mfma_bf16.restype = ctypes.c_int
+            _peaks = h
+    return _peaks
 
 
 def check(status: int, what: str) -> None:

@@ -1,12 +1,13 @@
-"""Build libsparse_attn.so (gfx950) in-tree with hipcc.
+"""Build libsparse_attn.so and libsa_peaks.so (gfx950) in-tree with hipcc.
 
     python -m block_sparse_attention_08_amd.build      # or build() from Python
 
 Compiles every ``csrc/*.hip`` to an object under ``_build/`` (in parallel) and
-links them into ``block_sparse_attention_08_amd/lib/libsparse_attn.so``.  The
-library links against the HIP runtime that torch ships, so that a process that
-imports torch first holds a single HIP runtime and torch's streams and device
-pointers are valid inside the library.
+links them into ``block_sparse_attention_08_amd/lib/libsparse_attn.so``; the
+measurement kernels under ``peaks/`` become ``lib/libsa_peaks.so``.  Both
+libraries link against the HIP runtime that torch ships, so that a process
+that imports torch first holds a single HIP runtime and torch's streams and
+device pointers are valid inside them.
 """
 
 from __future__ import annotations
@@ -24,6 +25,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 BUILD = os.path.join(ROOT, "_build")
 LIBNAME = "libsparse_attn.so"
+PEAKS_DIR = os.path.join(PKG, "peaks")
+PEAKS_LIBNAME = "libsa_peaks.so"
 ARCH = "gfx950"
 
 CXXFLAGS = [
@@ -58,13 +61,9 @@ def _run(cmd):
     return r.stdout + r.stderr
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile and link; returns the path of the shared library."""
+def _compile_and_link(srcs, tag, libname, verbose, jobs):
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    objs = [os.path.join(BUILD, tag + "_" + os.path.basename(s)[:-4] + ".o") for s in srcs]
 
     def one(pair):
         src, obj = pair
@@ -75,15 +74,26 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             if verbose and out.strip():
                 print(out)
 
-    link = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o",
-            os.path.join(LIBDIR, LIBNAME + ".tmp"), *objs]
+    tmp = os.path.join(LIBDIR, libname + ".tmp")
+    link = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     tl = _torch_lib_dir()
     if tl:
         # bind to torch's bundled HIP runtime (one runtime per process)
         link += [f"-L{tl}", f"-Wl,-rpath,{tl}", "-Wl,--disable-new-dtags"]
     _run(link)
-    os.replace(os.path.join(LIBDIR, LIBNAME + ".tmp"), os.path.join(LIBDIR, LIBNAME))
-    return os.path.join(LIBDIR, LIBNAME)
+    os.replace(tmp, os.path.join(LIBDIR, libname))
+    return os.path.join(LIBDIR, libname)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile and link both libraries; returns the path of libsparse_attn.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    path = _compile_and_link(sorted(glob.glob(os.path.join(CSRC, "*.hip"))), "sa", LIBNAME,
+                             verbose, jobs)
+    _compile_and_link(sorted(glob.glob(os.path.join(PEAKS_DIR, "*.hip"))), "peaks",
+                      PEAKS_LIBNAME, verbose, jobs)
+    return path
 
 
 if __name__ == "__main__":

@@ -22,9 +22,10 @@
 // K/V tiles move HBM -> LDS with buffer loads straight into LDS (range-
 // checked: rows past the last key read zero), XOR-swizzled per row (K:
 // chunk ^ (row & 15), V: chunk ^ 2*(row & 7) for d = 128) so the operand
-// reads are free of bank conflicts.  One K and one V buffer, two barriers per
-// tile: the next K tile loads during softmax and PV, the next V tile during
-// the next S.
+// reads are free of bank conflicts.  NBUF = 1: one K and one V buffer, two
+// barriers per tile (the next K tile loads during softmax and PV, the next V
+// tile during the next S).  NBUF = 2: two of each, one barrier per tile, the
+// next tile's K and V in flight through the whole current tile.
 #include <math.h>
 
 #include "attn_common.h"
@@ -102,11 +103,12 @@ __device__ __forceinline__ float row_sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int BLK>
+template <int D, int BLK, int NBUF>
 __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
   using C = Cfg<D, BLK>;
-  __shared__ __attribute__((aligned(1024))) char Ks[KT * D * 2];
-  __shared__ __attribute__((aligned(1024))) char Vs[KT * D * 2];
+  constexpr int TB = KT * D * 2;   // bytes of one K or V tile
+  __shared__ __attribute__((aligned(1024))) char Ks[NBUF * TB];
+  __shared__ __attribute__((aligned(1024))) char Vs[NBUF * TB];
   // one spare word: the tail mask reads the word after the tile's first
   __shared__ uint32_t selbits[kMaxBlocks / 32 + 1];
 
@@ -190,10 +192,10 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
     return (e - n_exact) * KT;
   };
   auto issue_k = [&](int e, int key0) {
-    dma_tile<D, BLK>(e < n_exact ? krs : tkrs, key0 * C::ROWB, Ks, w, koff);
+    dma_tile<D, BLK>(e < n_exact ? krs : tkrs, key0 * C::ROWB, Ks + (e % NBUF) * TB, w, koff);
   };
   auto issue_v = [&](int e, int key0) {
-    dma_tile<D, BLK>(e < n_exact ? vrs : tvrs, key0 * C::ROWB, Vs, w, voff);
+    dma_tile<D, BLK>(e < n_exact ? vrs : tvrs, key0 * C::ROWB, Vs + (e % NBUF) * TB, w, voff);
   };
 
   f32x4 o[C::NOT];
@@ -211,6 +213,14 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
 
   for (int e = 0; e < n_tiles; ++e) {
     const int key1 = e + 1 < n_tiles ? tile_key0(e + 1) : 0;
+    const char* Kc = Ks + (e % NBUF) * TB;
+    const char* Vc = Vs + (e % NBUF) * TB;
+    // NBUF = 2: buffer (e+1)%2 was last read in tile e-1, before the barrier
+    // that closed it
+    if (NBUF == 2 && e + 1 < n_tiles) {
+      issue_k(e + 1, key1);
+      issue_v(e + 1, key1);
+    }
 
     // ---- S^T = K Q^T (K operands read three steps ahead)
     f32x4 s[4];
@@ -220,7 +230,7 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
       bf16x8 kr[KD];
 #pragma unroll
       for (int i = 0; i < KD; ++i)
-        kr[i] = *reinterpret_cast<const bf16x8*>(Ks + kbase[i % C::NKS] + 16 * (i / C::NKS) * C::ROWB);
+        kr[i] = *reinterpret_cast<const bf16x8*>(Kc + kbase[i % C::NKS] + 16 * (i / C::NKS) * C::ROWB);
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -229,14 +239,16 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
         const bf16x8 ka = kr[step % KD];
         if (step + KD < NSTEP) {
           const int n2 = step + KD;
-          kr[step % KD] = *reinterpret_cast<const bf16x8*>(Ks + kbase[n2 % C::NKS] + 16 * (n2 / C::NKS) * C::ROWB);
+          kr[step % KD] = *reinterpret_cast<const bf16x8*>(Kc + kbase[n2 % C::NKS] + 16 * (n2 / C::NKS) * C::ROWB);
         }
         s[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], s[tg], 0, 0, 0);
       }
     }
-    wait_vm();
-    __syncthreads();                 // K buffer free, V tile e landed in every wave
-    if (e + 1 < n_tiles) issue_k(e + 1, key1);
+    if (NBUF == 1) {
+      wait_vm();
+      __syncthreads();               // K buffer free, V tile e landed in every wave
+      if (e + 1 < n_tiles) issue_k(e + 1, key1);
+    }
 
     // ---- masks: register r of key group tg holds key key0 + 16*tg + 4*lg + r
     if (e >= n_exact) {
@@ -307,7 +319,7 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
       constexpr int VD = 4;
       auto vop = [&](int j) -> bf16x8 {
         const int nt = j >> 1, cc = j & 1;
-        const char* p = Vs + vbase[nt] + (32 * cc) * C::ROWB;
+        const char* p = Vc + vbase[nt] + (32 * cc) * C::ROWB;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * C::ROWB));
         return __builtin_bit_cast(
@@ -325,8 +337,8 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
     }
 
     wait_vm();
-    __syncthreads();                 // V buffer free, K tile e+1 landed in every wave
-    if (e + 1 < n_tiles) issue_v(e + 1, key1);
+    __syncthreads();   // NBUF = 1: V buffer free, K tile e+1 landed; NBUF = 2: tile e+1 landed
+    if (NBUF == 1 && e + 1 < n_tiles) issue_v(e + 1, key1);
     key0 = key1;
   }
 
@@ -343,10 +355,13 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
   }
 }
 
+// 64-row blocks: four 4-wave workgroups per CU fit only single buffers;
+// 128-row blocks: two 8-wave workgroups per CU, double-buffered.
 template <int D, int BLK>
 hipError_t run(const Args& a, hipStream_t st) {
+  constexpr int NBUF = BLK == 128 ? 2 : 1;
   const int grid = 8 * ((a.total + 7) / 8);
-  hipLaunchKernelGGL((attn_w16_kernel<D, BLK>), dim3(grid), dim3(4 * BLK), 0, st, a);
+  hipLaunchKernelGGL((attn_w16_kernel<D, BLK, NBUF>), dim3(grid), dim3(4 * BLK), 0, st, a);
   return hipGetLastError();
 }
 

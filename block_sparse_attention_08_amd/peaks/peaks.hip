@@ -1,0 +1,100 @@
+// Achievable-rate kernels for the roofline denominators, measured on the
+// machine at hand next to the datasheet peaks: a streaming read over a buffer
+// much larger than the last-level cache (HBM), and a loop of independent bf16
+// matrix-core products (MFMA).  Measurement only; nothing on the attention
+// path calls them.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sa_peaks.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;                     // 16-byte loads in flight per thread and trip
+constexpr size_t kChunk = (size_t)kThreads * kUnroll * 16;   // bytes per workgroup trip
+
+// Workgroup w reads chunks w, w + grid, ...; thread t reads the vectors
+// t + 256u of a chunk.  The xor of everything read decides a store that never
+// happens, so no load can be dropped.
+__global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict__ p, size_t chunks,
+                                                        uint32_t* sink) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (size_t c = blockIdx.x; c < chunks; c += gridDim.x) {
+    const u32x4* q = p + c * (kThreads * kUnroll) + threadIdx.x;
+    u32x4 x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) x[u] = __builtin_nontemporal_load(q + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= x[u];
+  }
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[blockIdx.x & 255] = acc.x;
+}
+
+// Four independent accumulator chains per wave of v_mfma_f32_32x32x16_bf16
+// (32*32*16*2 flops each).  Operands depend on the lane and a runtime value,
+// the result decides a store that never happens.
+constexpr int kChains = 4;
+constexpr double kFlopsPerMfma = 32.0 * 32.0 * 16.0 * 2.0;
+
+__global__ __launch_bounds__(kThreads) void mfma_kernel(int iters, float seed, uint32_t* sink) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(seed * (float)(threadIdx.x + e));
+    b[e] = (__bf16)(seed * (float)(threadIdx.x - e));
+  }
+  f32x16 c[kChains];
+#pragma unroll
+  for (int i = 0; i < kChains; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[i][r] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < kChains; ++i) c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[i], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kChains; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c[i][r];
+  if (s == 1234.5f) sink[blockIdx.x & 255] = __float_as_uint(s);
+}
+
+int grid_for(int per_cu) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return cus * per_cu;
+}
+
+}  // namespace
+
+SA_PEAKS_EXPORT int sa_peak_read(const void* buf, size_t bytes, void* sink, void* stream,
+                                 size_t* bytes_read) {
+  if (!buf || !sink || !bytes_read) return (int)hipErrorInvalidValue;
+  if (((uintptr_t)buf & 15u) != 0) return (int)hipErrorInvalidValue;
+  const size_t chunks = bytes / kChunk;
+  *bytes_read = chunks * kChunk;
+  if (chunks == 0) return (int)hipSuccess;
+  const int grid = grid_for(8);
+  if (grid <= 0) return (int)hipErrorInvalidDevice;
+  hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const u32x4*)buf, chunks, (uint32_t*)sink);
+  return (int)hipGetLastError();
+}
+
+SA_PEAKS_EXPORT int sa_peak_mfma_bf16(int iters, void* sink, void* stream, double* flops) {
+  if (!sink || !flops || iters < 1) return (int)hipErrorInvalidValue;
+  const int grid = grid_for(8);
+  if (grid <= 0) return (int)hipErrorInvalidDevice;
+  *flops = (double)grid * (kThreads / 64) * (double)iters * kChains * kFlopsPerMfma;
+  hipLaunchKernelGGL(mfma_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, iters, 1.0e-3f,
+                     (uint32_t*)sink);
+  return (int)hipGetLastError();
+}

@@ -1,6 +1,6 @@
 """Workload definitions and seeded input draws.
 
-Five workloads, named by what they model:
+Six workloads, named by what they model:
 
 * ``dit_tiny_f32``    fp32, B=1, H=2,  N=1024,   d=64,  block 64, non-causal,
                       clustered keys (centre + 0.1 noise), alpha=0.5, tail on.
@@ -15,6 +15,9 @@ Five workloads, named by what they model:
                       alpha=0.5, no tail.
 * ``llm_prefill_256k`` bf16, B=1, H=8, N=262144, d=128, block 128, causal, same
                       generator as the 128K prefill, alpha=0.5, no tail.
+* ``llm_prefill_128k_tail`` the 128K prefill with the 0th-order tail on: the
+                      diagonal block is always exact, the tail covers the
+                      unselected blocks left of it.
 
 Every tensor is drawn in float32 from a numpy ``Generator`` seeded by
 ``SeedSequence([seed, workload tag, batch, kv group, stream])``, so one KV
@@ -74,6 +77,8 @@ CONFIGS: List[Workload] = [
              False, "sink"),
     Workload("llm_prefill_256k", "bf16", 1, 8, 8, 262144, 128, 128, True, "alpha", 0.5, 0.0,
              False, "sink"),
+    Workload("llm_prefill_128k_tail", "bf16", 1, 32, 8, 131072, 128, 128, True, "alpha", 0.5, 0.0,
+             True, "sink"),
 ]
 
 

@@ -45,6 +45,21 @@ def test_library_exports_every_declared_symbol():
     assert bsa.abi_version() == 2
 
 
+@pytest.mark.skipif(not os.path.exists(_lib.PEAKS_PATH), reason="libsa_peaks.so not built")
+def test_peaks_library_exports_and_rejects_bad_arguments():
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "sa_peaks.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(sa_peak_\w+)\s*\(", text)))
+    assert names == ["sa_peak_mfma_bf16", "sa_peak_read"]
+    h = _lib.peaks_lib()
+    for n in names:
+        assert hasattr(h, n), n
+    # argument errors come back before any device call (hipErrorInvalidValue = 1)
+    got = ctypes.c_size_t(7)
+    assert h.sa_peak_read(None, 1 << 20, None, None, ctypes.byref(got)) == 1
+    fl = ctypes.c_double(0.0)
+    assert h.sa_peak_mfma_bf16(0, ctypes.c_void_p(16), None, ctypes.byref(fl)) == 1
+
+
 @needs_lib
 def test_status_strings():
     h = _lib.lib()

@@ -23,6 +23,7 @@ CASES = [
     (1, 2, 2, 1000, 128, 64, "bf16", False, True, "alpha"),
     (1, 4, 2, 1300, 128, 128, "bf16", True, False, "alpha"),    # GQA, causal, 10*128 + 20
     (2, 2, 1, 700, 64, 64, "bf16", True, True, "alpha"),         # causal + tail (forced diagonal)
+    (1, 4, 2, 2600, 128, 128, "bf16", True, True, "alpha"),     # causal + tail, 128-row blocks, GQA
     (1, 2, 2, 900, 64, 128, "bf16", False, False, "density"),
     (1, 2, 2, 640, 64, 64, "f32", False, True, "alpha"),
     (1, 2, 1, 555, 128, 128, "f32", True, False, "density"),
