@@ -60,9 +60,8 @@
  *         dtype, written once by the pool pass for all query blocks
  *   blk_idx [batch, heads_q, M, M] int32: row (b,h,I) holds blk_cnt[b,h,I]
  *           strictly ascending eligible key-block indices; entries past the
- *           count are unspecified (sparse_attn_select uses the whole buffer
- *           as scratch for the M x M block scores before compacting each
- *           row in place; sparse_attn_fwd reads only the first count)
+ *           count are left untouched by sparse_attn_select and never read
+ *           by sparse_attn_fwd
  *   blk_cnt [batch, heads_q, M] int32, 1 <= count <= M
  *
  * Ownership and threading: the caller allocates and frees every buffer
@@ -141,9 +140,9 @@ sa_status sparse_attn_block_pool(const sa_desc* desc, const void* q, const void*
                                  const void* v, float* q_bar, float* k_bar, float* v_sum,
                                  void* tail, void* stream);
 
-/* Stage 2, scoring + selection: pooled scores (float32, held in blk_idx as
- * scratch), alpha-threshold or top-k selection, compaction of every row in
- * place into blk_idx / blk_cnt. */
+/* Stage 2, scoring + selection in one kernel: pooled scores (float32, kept
+ * on chip, never written), alpha-threshold or top-k selection, compaction of
+ * every row into blk_idx / blk_cnt. */
 sa_status sparse_attn_select(const sa_desc* desc, const float* q_bar, const float* k_bar,
                              int32_t* blk_idx, int32_t* blk_cnt, void* stream);
 
