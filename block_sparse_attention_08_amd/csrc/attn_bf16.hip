@@ -35,11 +35,10 @@
 // every lane picks the global 16-byte chunk that belongs at its LDS slot:
 // the LDS tiles are row-major with 16-byte chunks XOR-swizzled by row, which
 // keeps the MFMA operand reads free of bank conflicts without padding.
-// 128-row query blocks double-buffer K and V and software-pipeline: S of
-// tile e+1 sits next to the softmax of tile e, one barrier per tile.
-// 64-row blocks keep one K and one V buffer (four workgroups per CU): the
-// next K tile loads during this tile's softmax and PV, the next V tile
-// during the next S (two barriers per tile).  Tail tiles take the same path:
+// This kernel serves 128-row query blocks (64-row blocks go to the 16-row-
+// per-wave kernel): K and V are double-buffered and the loop is software-
+// pipelined -- S of tile e+1 sits next to the softmax of tile e, one barrier
+// per tile.  Tail tiles take the same path:
 // KT pooled rows of the bf16 block means of k and v that the pool pass
 // wrote once per head.
 // Workgroups are ordered so that each XCD receives a contiguous range of
@@ -237,47 +236,6 @@ __device__ __forceinline__ float softmax_max(State<D, BLK>& st, const f32x16 (&s
   return st.m == -INFINITY ? 0.f : st.m;
 }
 
-// Online softmax, part 2: P = exp2(S*c - mb) packed to bf16, row sums of
-// the packed values (dot2 with ones), and O^T += V^T P^T with V^T read by
-// LDS transpose loads.
-template <int D, int BLK>
-__device__ __forceinline__ void softmax_pv(State<D, BLK>& st, const f32x16 (&s)[2], const char* Vs,
-                                           const int (&vbase)[Cfg<D, BLK>::NOT], float c, float mb) {
-  using C = Cfg<D, BLK>;
-  bf16x8 pk[4];
-  float lsum = 0.f;
-#pragma unroll
-  for (int js = 0; js < 2; ++js) {
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      uint32_t wd[4];
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        const int r0 = 8 * h2 + 2 * q2;
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[js][r0], c, -mb));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[js][r0 + 1], c, -mb));
-        wd[q2] = pack2(p0, p1);
-        // row sum of the bf16-rounded P that the PV product uses
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[q2]), kOnes, lsum, false);
-      }
-      pk[2 * js + h2] = __builtin_bit_cast(bf16x8, u32x4{wd[0], wd[1], wd[2], wd[3]});
-    }
-  }
-  st.l += lsum;
-
-  constexpr int VD = 4;
-  constexpr int NPV = 4 * C::NOT;
-  bf16x8 vr[VD];
-#pragma unroll
-  for (int j = 0; j < VD; ++j) vr[j] = v_operand<D, BLK>(Vs, vbase, j / 4, j % 4);
-#pragma unroll
-  for (int j = 0; j < NPV; ++j) {
-    const bf16x8 va = vr[j % VD];
-    if (j + VD < NPV) vr[j % VD] = v_operand<D, BLK>(Vs, vbase, (j + VD) / 4, (j + VD) % 4);
-    st.o[j / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[j % 4], st.o[j / 4], 0, 0, 0);
-  }
-}
-
 // S^T = K Q^T for one 64-key tile held in LDS (K operands read 3 ahead).
 template <int D, int BLK>
 __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const char* Ks, const int (&kbase)[Cfg<D, BLK>::NKS],
@@ -369,12 +327,16 @@ __device__ __forceinline__ void pipe_step(State<D, BLK>& st, const f32x16 (&s)[2
 template <int D, int BLK>
 __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
   using C = Cfg<D, BLK>;
-  // K and V tile buffers: tile e uses buffer e % NBUF.  128-row query
-  // blocks double-buffer (software pipeline, one barrier per tile); 64-row
-  // blocks single-buffer, which keeps 4 two-wave workgroups per CU.
-  constexpr int NBUF = BLK == 128 ? 2 : 1;
-  __shared__ __attribute__((aligned(1024))) char Ks[NBUF][KT * D * 2];
-  __shared__ __attribute__((aligned(1024))) char Vs[NBUF][KT * D * 2];
+  static_assert(BLK == 128, "64-row query blocks use the 16-row-per-wave kernel");
+  // Double-buffered K and V tiles: tile e uses buffers K[e & 1], V[e & 1].
+  // Four separate LDS objects, each named statically in every unrolled tile
+  // step: the compiler can then tell that the transposed V reads of one
+  // buffer do not overlap the tile loads in flight into the other, and does
+  // not make the reads wait for those loads.
+  __shared__ __attribute__((aligned(1024))) char K0[KT * D * 2];
+  __shared__ __attribute__((aligned(1024))) char K1[KT * D * 2];
+  __shared__ __attribute__((aligned(1024))) char V0[KT * D * 2];
+  __shared__ __attribute__((aligned(1024))) char V1[KT * D * 2];
   // one spare word: the tail mask reads the word after the tile's first
   __shared__ uint32_t selbits[kMaxBlocks / 32 + 1];
 
@@ -411,8 +373,8 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
     }
   }
 
-  const int n_sel = a.cnt[(size_t)bh * a.M + I];
-  const int32_t* list = a.idx + ((size_t)bh * a.M + I) * a.M;
+  const int n_sel = scalar_view(a.cnt)[(size_t)bh * a.M + I];
+  const const_i32* list = scalar_view(a.idx + ((size_t)bh * a.M + I) * a.M);
   const int Jend = a.causal ? I + 1 : a.M;
   const int n_exact = n_sel * C::SUB;
   const int n_tiles = n_exact + (a.approx ? (Jend + KT - 1) / KT : 0);
@@ -466,11 +428,11 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
   }
   // exact tiles: KT keys of the head; tail tiles: KT pooled rows (bf16 block
   // means of k and of v from the pool pass), both straight into LDS
-  auto issue_k = [&](int e, int key0) {
-    dma_tile<D, BLK>(e < n_exact ? krs : tkrs, key0 * C::ROWB, Ks[e % NBUF], w, koff);
+  auto issue_k = [&](int e, int key0, char* dst) {
+    dma_tile<D, BLK>(e < n_exact ? krs : tkrs, key0 * C::ROWB, dst, w, koff);
   };
-  auto issue_v = [&](int e, int key0) {
-    dma_tile<D, BLK>(e < n_exact ? vrs : tvrs, key0 * C::ROWB, Vs[e % NBUF], w, voff);
+  auto issue_v = [&](int e, int key0, char* dst) {
+    dma_tile<D, BLK>(e < n_exact ? vrs : tvrs, key0 * C::ROWB, dst, w, voff);
   };
 
   State<D, BLK> st;
@@ -494,62 +456,42 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
     }
   };
 
-  if constexpr (NBUF == 2) {
-    // Pipeline: while the softmax of tile e runs on the vector ALUs, the
-    // matrix cores compute S of tile e+1; K e+2 and V e+1 load meanwhile.
-    // One barrier per tile: it retires tile e's buffers and publishes the
-    // loads issued during it.
-    int key0 = tile_key0(0);
-    int key1 = n_tiles > 1 ? tile_key0(1) : 0;
-    issue_k(0, key0);
-    issue_v(0, key0);
-    if (n_tiles > 1) issue_k(1, key1);
-    wait_vm();
-    __syncthreads();
-    f32x16 s[2];
-    qk_tile<D, BLK>(s, Ks[0], kbase, qf);
+  // Pipeline: while the softmax of tile e runs on the vector ALUs, the
+  // matrix cores compute S of tile e+1; K e+2 and V e+1 load meanwhile.
+  // One barrier per tile: it retires tile e's buffers and publishes the
+  // loads issued during it.
+  int key0 = tile_key0(0);
+  int key1 = n_tiles > 1 ? tile_key0(1) : 0;
+  issue_k(0, key0, K0);
+  issue_v(0, key0, V0);
+  if (n_tiles > 1) issue_k(1, key1, K1);
+  wait_vm();
+  __syncthreads();
+  f32x16 s[2];
+  qk_tile<D, BLK>(s, K0, kbase, qf);
 
-    for (int e = 0; e < n_tiles; ++e) {
-      const int cur = e & 1;
-      const int key2 = e + 2 < n_tiles ? tile_key0(e + 2) : 0;
-      if (e + 1 < n_tiles) issue_v(e + 1, key1);
-      if (e + 2 < n_tiles) issue_k(e + 2, key2);
-      mask_tile(s, e, key0);
-      const float mb = softmax_max<D, BLK>(st, s, c);
-      // S of tile e+1 (on the last tile this reads a retired buffer and the
-      // result is dropped) interleaved with the softmax of tile e
-      f32x16 s_next[2];
-      pipe_step<D, BLK>(st, s, s_next, Ks[cur ^ 1], Vs[cur], kbase, vbase, qf, c, mb);
-      wait_vm();
-      __syncthreads();
-#pragma unroll
-      for (int js = 0; js < 2; ++js) s[js] = s_next[js];
-      key0 = key1;
-      key1 = key2;
-    }
-  } else {
-    // Single buffers, two barriers per tile: K e+1 loads during the softmax
-    // and PV of tile e, V e+1 during S of tile e+1.
-    int key0 = tile_key0(0);
-    issue_k(0, key0);
-    issue_v(0, key0);
+  // one tile step; Kn holds tile e+1 (read now) and receives tile e+2, Vc
+  // holds tile e, Vn receives tile e+1
+  auto step = [&](int e, const char* Kn, char* Kc, const char* Vc, char* Vn) __attribute__((always_inline)) {
+    const int key2 = e + 2 < n_tiles ? tile_key0(e + 2) : 0;
+    if (e + 1 < n_tiles) issue_v(e + 1, key1, Vn);
+    if (e + 2 < n_tiles) issue_k(e + 2, key2, Kc);
+    mask_tile(s, e, key0);
+    const float mb = softmax_max<D, BLK>(st, s, c);
+    // S of tile e+1 (on the last tile this reads a retired buffer and the
+    // result is dropped) interleaved with the softmax of tile e
+    f32x16 s_next[2];
+    pipe_step<D, BLK>(st, s, s_next, Kn, Vc, kbase, vbase, qf, c, mb);
     wait_vm();
     __syncthreads();
-    for (int e = 0; e < n_tiles; ++e) {
-      const int key1 = e + 1 < n_tiles ? tile_key0(e + 1) : 0;
-      f32x16 s[2];
-      qk_tile<D, BLK>(s, Ks[0], kbase, qf);
-      wait_vm();
-      __syncthreads();                 // K buffer free, V tile e landed in every wave
-      if (e + 1 < n_tiles) issue_k(e + 1, key1);
-      mask_tile(s, e, key0);
-      const float mb = softmax_max<D, BLK>(st, s, c);
-      softmax_pv<D, BLK>(st, s, Vs[0], vbase, c, mb);
-      wait_vm();
-      __syncthreads();                 // V buffer free, K tile e+1 landed in every wave
-      if (e + 1 < n_tiles) issue_v(e + 1, key1);
-      key0 = key1;
-    }
+#pragma unroll
+    for (int js = 0; js < 2; ++js) s[js] = s_next[js];
+    key0 = key1;
+    key1 = key2;
+  };
+  for (int e = 0; e < n_tiles; e += 2) {
+    step(e, K1, K0, V0, V1);
+    if (e + 1 < n_tiles) step(e + 1, K0, K1, V1, V0);
   }
 
   // ---- epilogue: O / l, bf16, row q_tok; register r of d-tile nt holds
@@ -607,8 +549,7 @@ hipError_t launch_fwd(const Shape& s, const FwdParams& p, const void* q, const v
   a.scale_log2 = p.scale * 1.4426950408889634f;
   a.causal = p.causal;
   a.approx = p.approx;
-  if (s.D == 128) return s.block == 128 ? run<128, 128>(a, st) : run<128, 64>(a, st);
-  return s.block == 128 ? run<64, 128>(a, st) : run<64, 64>(a, st);
+  return s.D == 128 ? run<128, 128>(a, st) : run<64, 128>(a, st);
 }
 
 }  // namespace sa

@@ -22,10 +22,9 @@
 // K/V tiles move HBM -> LDS with buffer loads straight into LDS (range-
 // checked: rows past the last key read zero), XOR-swizzled per row (K:
 // chunk ^ (row & 15), V: chunk ^ 2*(row & 7) for d = 128) so the operand
-// reads are free of bank conflicts.  NBUF = 1: one K and one V buffer, two
-// barriers per tile (the next K tile loads during softmax and PV, the next V
-// tile during the next S).  NBUF = 2: two of each, one barrier per tile, the
-// next tile's K and V in flight through the whole current tile.
+// reads are free of bank conflicts.  One K and one V buffer, two barriers per
+// tile (the next K tile loads during softmax and PV, the next V tile during
+// the next S).  Serves 64-row query blocks only.
 #include <math.h>
 
 #include "attn_common.h"
@@ -103,12 +102,13 @@ __device__ __forceinline__ float row_sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, int BLK, int NBUF>
+template <int D, int BLK>
 __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
   using C = Cfg<D, BLK>;
+  static_assert(BLK == KT, "one 64-key tile per block");
   constexpr int TB = KT * D * 2;   // bytes of one K or V tile
-  __shared__ __attribute__((aligned(1024))) char Ks[NBUF * TB];
-  __shared__ __attribute__((aligned(1024))) char Vs[NBUF * TB];
+  __shared__ __attribute__((aligned(1024))) char Ks[TB];
+  __shared__ __attribute__((aligned(1024))) char Vs[TB];
   // one spare word: the tail mask reads the word after the tile's first
   __shared__ uint32_t selbits[kMaxBlocks / 32 + 1];
 
@@ -143,11 +143,10 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
     }
   }
 
-  const int n_sel = a.cnt[(size_t)bh * a.M + I];
-  const int32_t* list = a.idx + ((size_t)bh * a.M + I) * a.M;
+  const int n_sel = scalar_view(a.cnt)[(size_t)bh * a.M + I];
+  const const_i32* list = scalar_view(a.idx + ((size_t)bh * a.M + I) * a.M);
   const int Jend = a.causal ? I + 1 : a.M;
-  constexpr int SUB = BLK / KT;
-  const int n_exact = n_sel * SUB;
+  const int n_exact = n_sel;
   const int n_tiles = n_exact + (a.approx ? (Jend + KT - 1) / KT : 0);
   const int last_n = a.N - (a.M - 1) * BLK;
   const float bias_blk = __log2f((float)BLK) / a.scale_log2;
@@ -187,15 +186,14 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
     }
   }
 
-  auto tile_key0 = [&](int e) -> int {
-    if (e < n_exact) return list[e / SUB] * BLK + (e % SUB) * KT;
-    return (e - n_exact) * KT;
-  };
+  // first key (token, or pooled row for tail tiles) of tile e; one 64-key
+  // tile per listed block
+  auto tile_key0 = [&](int e) -> int { return e < n_exact ? list[e] * BLK : (e - n_exact) * KT; };
   auto issue_k = [&](int e, int key0) {
-    dma_tile<D, BLK>(e < n_exact ? krs : tkrs, key0 * C::ROWB, Ks + (e % NBUF) * TB, w, koff);
+    dma_tile<D, BLK>(e < n_exact ? krs : tkrs, key0 * C::ROWB, Ks, w, koff);
   };
   auto issue_v = [&](int e, int key0) {
-    dma_tile<D, BLK>(e < n_exact ? vrs : tvrs, key0 * C::ROWB, Vs + (e % NBUF) * TB, w, voff);
+    dma_tile<D, BLK>(e < n_exact ? vrs : tvrs, key0 * C::ROWB, Vs, w, voff);
   };
 
   f32x4 o[C::NOT];
@@ -205,22 +203,13 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
   float l = 0.f;         // this lane's partial row sum
   const float c = a.scale_log2;
 
-  int key0 = tile_key0(0);
-  issue_k(0, key0);
-  issue_v(0, key0);
-  wait_vm();
-  __syncthreads();
-
-  for (int e = 0; e < n_tiles; ++e) {
-    const int key1 = e + 1 < n_tiles ? tile_key0(e + 1) : 0;
-    const char* Kc = Ks + (e % NBUF) * TB;
-    const char* Vc = Vs + (e % NBUF) * TB;
-    // NBUF = 2: buffer (e+1)%2 was last read in tile e-1, before the barrier
-    // that closed it
-    if (NBUF == 2 && e + 1 < n_tiles) {
-      issue_k(e + 1, key1);
-      issue_v(e + 1, key1);
-    }
+  // One tile: S, masks, online softmax, PV.  MODE says which masks the tile
+  // needs (a separate copy of the body per mode keeps the unmasked tiles free
+  // of mask code and of the register copies a conditional mask would cause).
+  // One K and one V buffer, two barriers: K e+1 loads during the softmax and
+  // PV of tile e, V e+1 during S of tile e+1.
+  auto step = [&](int e, int key0, int key1, auto mode) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode)::value;
 
     // ---- S^T = K Q^T (K operands read three steps ahead)
     f32x4 s[4];
@@ -230,28 +219,26 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
       bf16x8 kr[KD];
 #pragma unroll
       for (int i = 0; i < KD; ++i)
-        kr[i] = *reinterpret_cast<const bf16x8*>(Kc + kbase[i % C::NKS] + 16 * (i / C::NKS) * C::ROWB);
+        kr[i] = *reinterpret_cast<const bf16x8*>(Ks + kbase[i % C::NKS] + 16 * (i / C::NKS) * C::ROWB);
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int step = 0; step < NSTEP; ++step) {
-        const int tg = step / C::NKS, ks = step % C::NKS;
-        const bf16x8 ka = kr[step % KD];
-        if (step + KD < NSTEP) {
-          const int n2 = step + KD;
-          kr[step % KD] = *reinterpret_cast<const bf16x8*>(Kc + kbase[n2 % C::NKS] + 16 * (n2 / C::NKS) * C::ROWB);
+      for (int st = 0; st < NSTEP; ++st) {
+        const int tg = st / C::NKS, ks = st % C::NKS;
+        const bf16x8 ka = kr[st % KD];
+        if (st + KD < NSTEP) {
+          const int n2 = st + KD;
+          kr[st % KD] = *reinterpret_cast<const bf16x8*>(Ks + kbase[n2 % C::NKS] + 16 * (n2 / C::NKS) * C::ROWB);
         }
         s[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], s[tg], 0, 0, 0);
       }
     }
-    if (NBUF == 1) {
-      wait_vm();
-      __syncthreads();               // K buffer free, V tile e landed in every wave
-      if (e + 1 < n_tiles) issue_k(e + 1, key1);
-    }
+    wait_vm();
+    __syncthreads();               // K buffer free, V tile e landed in every wave
+    if (e + 1 < n_tiles) issue_k(e + 1, key1);
 
     // ---- masks: register r of key group tg holds key key0 + 16*tg + 4*lg + r
-    if (e >= n_exact) {
+    if constexpr (MODE == kModeTail) {
       const int lim = Jend - key0 - 4 * lg;
       const int last_kr = a.M - 1 - key0 - 4 * lg;
       const uint32_t w0 = selbits[key0 >> 5] >> (4 * lg);
@@ -266,7 +253,7 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
           s[tg][r] = on ? s[tg][r] + (kr == last_kr ? bias_last : bias_blk) : -INFINITY;
         }
       }
-    } else if (key0 + KT > a.N || (a.causal && key0 + KT > I * BLK)) {
+    } else if constexpr (MODE == kModeEdge) {
       int lim = a.N - key0;
       if (a.causal) lim = min(lim, q_tok - key0 + 1);
       lim -= 4 * lg;
@@ -319,7 +306,7 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
       constexpr int VD = 4;
       auto vop = [&](int j) -> bf16x8 {
         const int nt = j >> 1, cc = j & 1;
-        const char* p = Vc + vbase[nt] + (32 * cc) * C::ROWB;
+        const char* p = Vs + vbase[nt] + (32 * cc) * C::ROWB;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * C::ROWB));
         return __builtin_bit_cast(
@@ -337,8 +324,38 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
     }
 
     wait_vm();
-    __syncthreads();   // NBUF = 1: V buffer free, K tile e+1 landed; NBUF = 2: tile e+1 landed
-    if (NBUF == 1 && e + 1 < n_tiles) issue_v(e + 1, key1);
+    __syncthreads();   // V buffer free, K tile e+1 landed in every wave
+    if (e + 1 < n_tiles) issue_v(e + 1, key1);
+  };
+
+  int key0 = tile_key0(0);
+  issue_k(0, key0);
+  issue_v(0, key0);
+  wait_vm();
+  __syncthreads();
+
+  // Only the ragged last block (J = M-1) and the causal diagonal (J = I)
+  // need the edge mask; either is the largest index a list may hold, so in
+  // an ascending list it can only be the last entry.
+  int n_plain = n_exact;
+  if (n_exact > 0) {
+    const int J = list[n_exact - 1];
+    if ((J + 1) * BLK > a.N || (a.causal && J >= I)) n_plain = n_exact - 1;
+  }
+  int e = 0;
+  for (; e < n_plain; ++e) {
+    const int key1 = e + 1 < n_tiles ? tile_key0(e + 1) : 0;
+    step(e, key0, key1, ModeC<kModePlain>{});
+    key0 = key1;
+  }
+  for (; e < n_exact; ++e) {
+    const int key1 = e + 1 < n_tiles ? tile_key0(e + 1) : 0;
+    step(e, key0, key1, ModeC<kModeEdge>{});
+    key0 = key1;
+  }
+  for (; e < n_tiles; ++e) {
+    const int key1 = e + 1 < n_tiles ? tile_key0(e + 1) : 0;
+    step(e, key0, key1, ModeC<kModeTail>{});
     key0 = key1;
   }
 
@@ -355,13 +372,11 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
   }
 }
 
-// 64-row blocks: four 4-wave workgroups per CU fit only single buffers;
-// 128-row blocks: two 8-wave workgroups per CU, double-buffered.
-template <int D, int BLK>
+// 64-row blocks: four 4-wave workgroups per CU (32 KB of tile buffers each).
+template <int D>
 hipError_t run(const Args& a, hipStream_t st) {
-  constexpr int NBUF = BLK == 128 ? 2 : 1;
   const int grid = 8 * ((a.total + 7) / 8);
-  hipLaunchKernelGGL((attn_w16_kernel<D, BLK, NBUF>), dim3(grid), dim3(4 * BLK), 0, st, a);
+  hipLaunchKernelGGL((attn_w16_kernel<D, 64>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -390,8 +405,8 @@ hipError_t launch_fwd_w16(const Shape& s, const FwdParams& p, const void* q, con
   a.scale_log2 = p.scale * 1.4426950408889634f;
   a.causal = p.causal;
   a.approx = p.approx;
-  if (s.D == 128) return s.block == 128 ? run<128, 128>(a, st) : run<128, 64>(a, st);
-  return s.block == 128 ? run<64, 128>(a, st) : run<64, 64>(a, st);
+  if (s.block != 64) return hipErrorInvalidValue;
+  return s.D == 128 ? run<128>(a, st) : run<64>(a, st);
 }
 
 }  // namespace sa

@@ -18,6 +18,12 @@ constexpr int KT = 64;  // keys per tile (a 128-token block is two tiles)
 
 constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
+// Masking a tile needs: none (interior exact tile), the ragged end / causal
+// diagonal (edge), or the tail rules (pooled rows).
+enum { kModePlain = 0, kModeEdge = 1, kModeTail = 2 };
+template <int MODE>
+struct ModeC { static constexpr int value = MODE; };
+
 // two floats -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
@@ -26,6 +32,15 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // Wait until this wave's outstanding global loads (including the ones that
 // write LDS directly) have completed.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// The block lists and counts stay unchanged while an attention kernel runs:
+// reading them through the constant address space turns the uniform per-tile
+// index reads into scalar loads, counted by lgkmcnt, so that fetching the
+// next block index never waits on the K/V tile loads in flight (vmcnt).
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+__device__ __forceinline__ const const_i32* scalar_view(const int32_t* p) {
+  return (const const_i32*)p;
+}
 
 // Buffer resource over one [rows, D] bf16 head of `bytes` bytes: loads past
 // the end return zero (rows of a ragged last block, pooled rows past M).
