@@ -15,13 +15,14 @@
 //   section 2, online softmax), answer o / l.
 //
 // Mapping: one workgroup per (batch, head, query block) with block/32 waves;
-// wave w owns 32 query rows.  Per key tile (one block of `block` keys, or
-// `block` pooled rows for the tail):
+// wave w owns 32 query rows.  Keys are visited in tiles of KT = block/2 keys
+// (two tiles per listed block; a tail tile is KT pooled rows).  Per tile:
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16; A = K tile rows read from LDS,
 //                 B = the wave's Q rows (registers for the whole kernel).
 //                 The accumulator holds one query row per lane (lanes l and
-//                 l+32 share row l%32, 16 keys each), so the row max needs
-//                 one cross-lane exchange and the softmax state is per lane.
+//                 l+32 share row l%32, 16 keys each per 32-key group), so the
+//                 row max needs one cross-lane exchange and the softmax state
+//                 is per lane.
 //   P = exp2(S*scale*log2e - m), packed to bf16 in place: these registers are
 //                 directly the B operand of the next product.
 //   O^T += V^T P^T  A = V^T fragments gathered from the row-major V tile with
@@ -34,13 +35,20 @@
 // the last key.  Each wave instruction fills 1 KB of LDS contiguously, so
 // every lane picks the global 16-byte chunk that belongs at its LDS slot:
 // the LDS tiles are row-major with 16-byte chunks XOR-swizzled by row, which
-// keeps the MFMA operand reads free of bank conflicts without padding.
-// This kernel serves 128-row query blocks (64-row blocks go to the 16-row-
-// per-wave kernel): K and V are double-buffered and the loop is software-
-// pipelined -- S of tile e+1 sits next to the softmax of tile e, one barrier
-// per tile.  Tail tiles take the same path:
-// KT pooled rows of the bf16 block means of k and v that the pool pass
-// wrote once per head.
+// keeps the MFMA operand reads free of bank conflicts without padding.  Tail
+// tiles gather their pooled rows (bf16 block means of k and v, written once
+// per head by the pool pass) by per-lane row offsets from the list of
+// unlisted eligible blocks, built in LDS at the start.
+//
+// K and V are double-buffered and the loop is software-pipelined: S of tile
+// e+1 sits next to the softmax of tile e, one barrier per tile.  Tiles that
+// need masks (the ragged last block, the causal diagonal, the partly filled
+// last tail tile) are visited last, so the main loop carries no mask code;
+// the order of the tiles does not change the softmax.
+// 128-row blocks: four waves, 64-key tiles, 64 KB of tile buffers, two
+// workgroups per CU.  (The template also builds 64-row blocks as two waves
+// over 32-key tiles; measured slower than the 16-row-per-wave kernel on the
+// 8K image workload, faster on the 32K video one, it is not dispatched.)
 // Workgroups are ordered so that each XCD receives a contiguous range of
 // (kv head, query block) items, with the query heads of one KV group
 // adjacent, so K/V blocks shared by neighbouring items stay in one L2.
@@ -80,12 +88,15 @@ template <int D, int BLK>
 struct Cfg {
   static constexpr int NW = BLK / 32;         // waves
   static constexpr int NT = 64 * NW;          // threads
+  static constexpr int T = BLK / 2;           // keys per tile (two tiles per block)
+  static constexpr int NJS = T / 32;          // 32-key groups of S^T per tile
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
-  static constexpr int NI = KT * CPR / NT;    // 16-byte loads per thread per tile
+  static constexpr int NI = T * CPR / NT;     // 16-byte DMA loads per thread per tile
   static constexpr int NKS = D / 16;          // 16-wide d steps of S
   static constexpr int NOT = D / 32;          // 32-wide d tiles of O
   static constexpr int ROWB = D * 2;          // bytes per LDS row
-  static constexpr int SUB = BLK / KT;        // tiles per key block
+  static constexpr int RPK = 1024 / ROWB;     // rows filled by one 1 KB DMA instruction
+  static constexpr int TB = T * ROWB;         // bytes of one K or V tile
   static_assert(NI >= 1, "tile smaller than the workgroup");
 };
 
@@ -111,44 +122,56 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-
-
-// Byte offset, inside a KT x D tile, of the global 16-byte chunk this lane
-// copies with direct load i: instruction i of wave w fills LDS chunks
-// (i*NW + w)*64 + lane, so rows advance by whole KB per instruction and the
-// lane's swizzle repeats with period NVAR in i (the swizzle period in rows
-// over the rows per KB, divided by the waves).  Instruction i reads
-// lane_off[i % NVAR] + i*NW*1024.
+// DMA lane layout: instruction i of wave w fills LDS chunks (i*NW + w)*64 +
+// lane of the tile, i.e. row r_i = (i*NW + w)*RPK + lane/CPR, chunk slot
+// lane%CPR.  The lane copies the global chunk that the swizzle places in that
+// slot; its column offset repeats with period NVAR in i (the swizzle period
+// in rows over the rows one instruction step advances).
 template <int D, int BLK>
 struct DmaCfg {
-  static constexpr int ROWS_PER_KB = 1024 / (2 * D);
+  using C = Cfg<D, BLK>;
   static constexpr int PERIOD = D == 128 ? 16 : 8;            // K swizzle period in rows
-  static constexpr int STEP = Cfg<D, BLK>::NW * ROWS_PER_KB;  // rows per instruction step
+  static constexpr int STEP = C::NW * C::RPK;                 // rows per instruction step
   static constexpr int NVAR = STEP % PERIOD == 0 ? 1 : PERIOD / STEP;
 };
 
+// Column byte offset (swizzled chunk * 16) of this lane's chunk for
+// instruction i (i < NVAR).
 template <int D, int BLK, bool IS_V>
-__device__ __forceinline__ int dma_lane_off(int i, int w, int lane) {
+__device__ __forceinline__ int dma_col(int i, int w, int lane) {
   using C = Cfg<D, BLK>;
-  const int P = (i * C::NW + w) * 64 + lane;
-  const int r = P / C::CPR, pc = P % C::CPR;
-  const int c = IS_V ? v_chunk<D>(r, pc) : k_chunk<D>(r, pc);
-  return (r - i * C::NW * DmaCfg<D, BLK>::ROWS_PER_KB) * C::ROWB + c * 16;
+  const int r = (i * C::NW + w) * C::RPK + lane / C::CPR;
+  const int pc = lane % C::CPR;
+  return (IS_V ? v_chunk<D>(r, pc) : k_chunk<D>(r, pc)) * 16;
 }
 
-
-// Direct HBM -> LDS load of one exact K or V tile: KT rows starting at byte
-// `tile_off` of the head.
+// One K or V tile: T consecutive rows from byte `tile_off` of the head.
 template <int D, int BLK>
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int tile_off, char* lds, int w,
-                                         const int (&lane_off)[DmaCfg<D, BLK>::NVAR]) {
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int tile_off, char* lds, int w, int row0,
+                                         const int (&col)[DmaCfg<D, BLK>::NVAR]) {
   using C = Cfg<D, BLK>;
 #pragma unroll
   for (int i = 0; i < C::NI; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (i * C::NW + w) * 1024), 16,
-                                             lane_off[i % DmaCfg<D, BLK>::NVAR],
+                                             row0 * C::ROWB + col[i % DmaCfg<D, BLK>::NVAR],
                                              tile_off + i * C::NW * 1024, 0, 0);
 }
+
+// Gathered tile: instruction i copies this lane's chunk of the row at byte
+// offset ro[i] (the pooled rows of a tail tile).
+template <int D, int BLK>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, const int (&ro)[Cfg<D, BLK>::NI], char* lds,
+                                         int w, const int (&col)[DmaCfg<D, BLK>::NVAR]) {
+  using C = Cfg<D, BLK>;
+#pragma unroll
+  for (int i = 0; i < C::NI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (i * C::NW + w) * 1024), 16,
+                                             ro[i] + col[i % DmaCfg<D, BLK>::NVAR], 0, 0, 0);
+}
+
+// S^T accumulators of one tile
+template <int D, int BLK>
+using SAcc = f32x16[Cfg<D, BLK>::NJS];
 
 template <int D, int BLK>
 struct State {
@@ -160,34 +183,6 @@ struct State {
 // Register r of the S^T accumulator s[js] holds key key0 + 32*js + 8*(r/4)
 // + 4*hh + (r%4) of the tile; kr(js, r) is that key minus key0 + 4*hh.
 __device__ __forceinline__ constexpr int kr_of(int js, int r) { return 32 * js + 8 * (r >> 2) + (r & 3); }
-
-// Exact tile at the end of the sequence or on the causal diagonal: keys with
-// kr >= lim are masked.
-__device__ __forceinline__ void mask_exact(f32x16 (&s)[2], int lim) {
-#pragma unroll
-  for (int js = 0; js < 2; ++js)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[js][r] = kr_of(js, r) < lim ? s[js][r] : -INFINITY;
-}
-
-// Tail tile (pooled rows): rows past the eligible range or in the selected
-// set are masked; the others get the logit offset log2(n_J)/(scale*log2 e)
-// so that exp2 of the scaled logit is n_J * exp(q.kbar_J): the pseudo-key's
-// multiplicity.  `word` holds the selection bits of the 32 rows from
-// key0 + 32*js, shifted by 4*hh.
-__device__ __forceinline__ void mask_tail(f32x16 (&s)[2], int lim, uint32_t w0, uint32_t w1,
-                                          int last_kr, float bias, float bias_last) {
-#pragma unroll
-  for (int js = 0; js < 2; ++js) {
-    const uint32_t word = js ? w1 : w0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kr = kr_of(js, r);
-      const bool on = kr < lim && !((word >> (kr - 32 * js)) & 1u);
-      s[js][r] = on ? s[js][r] + (kr == last_kr ? bias_last : bias) : -INFINITY;
-    }
-  }
-}
 
 // V^T operand of PV step (nt, kc): two LDS transpose reads.
 template <int D, int BLK>
@@ -208,19 +203,21 @@ __device__ __forceinline__ bf16x8 k_operand(const char* Ks, const int (&kbase)[C
   return *reinterpret_cast<const bf16x8*>(Ks + kbase[ks] + 32 * js * C::ROWB);
 }
 
-// Online softmax, part 1, for one 64-key tile (S^T accumulators s[0], s[1],
-// already masked): running max with lazy rescale of O and l.  Returns the
-// reference max (0 while no key has been seen) for the exponentials.
+// Online softmax, part 1, for one tile (S^T accumulators, already masked):
+// running max with lazy rescale of O and l.  lb is added to every logit of
+// the tile (log2 n_J for tail rows).  Returns the reference max minus lb (lb
+// while no key has been seen) for the exponentials.
 template <int D, int BLK>
-__device__ __forceinline__ float softmax_max(State<D, BLK>& st, const f32x16 (&s)[2], float c) {
+__device__ __forceinline__ float softmax_max(State<D, BLK>& st, const SAcc<D, BLK>& s, float c,
+                                             float lb) {
   using C = Cfg<D, BLK>;
   float mx = -INFINITY;
 #pragma unroll
-  for (int js = 0; js < 2; ++js)
+  for (int js = 0; js < C::NJS; ++js)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[js][r]);
   mx = half_max(mx);
-  const float mxs = mx * c;
+  const float mxs = fmaf(mx, c, lb);
   const bool grow = mxs > st.m + 8.f;
   if (__ballot(grow)) {
     const float m_new = grow ? mxs : st.m;
@@ -233,18 +230,19 @@ __device__ __forceinline__ float softmax_max(State<D, BLK>& st, const f32x16 (&s
     }
     st.m = m_new;
   }
-  return st.m == -INFINITY ? 0.f : st.m;
+  return (st.m == -INFINITY ? 0.f : st.m) - lb;
 }
 
-// S^T = K Q^T for one 64-key tile held in LDS (K operands read 3 ahead).
+// S^T = K Q^T for one tile held in LDS (K operands read 3 ahead).
 template <int D, int BLK>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const char* Ks, const int (&kbase)[Cfg<D, BLK>::NKS],
+__device__ __forceinline__ void qk_tile(SAcc<D, BLK>& s, const char* Ks,
+                                        const int (&kbase)[Cfg<D, BLK>::NKS],
                                         const bf16x8 (&qf)[Cfg<D, BLK>::NKS]) {
   using C = Cfg<D, BLK>;
-  constexpr int NSTEP = 2 * C::NKS;
+  constexpr int NSTEP = C::NJS * C::NKS;
   constexpr int KD = 3;
-  s[0] = f32x16{};
-  s[1] = f32x16{};
+#pragma unroll
+  for (int js = 0; js < C::NJS; ++js) s[js] = f32x16{};
   bf16x8 kr[KD];
 #pragma unroll
   for (int i = 0; i < KD; ++i) kr[i] = k_operand<D, BLK>(Ks, kbase, i);
@@ -264,22 +262,24 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const char* Ks, const in
 // exponentials ahead of the products, so the matrix cores and the vector
 // ALUs work side by side.
 template <int D, int BLK>
-__device__ __forceinline__ void pipe_step(State<D, BLK>& st, const f32x16 (&s)[2], f32x16 (&s_next)[2],
-                                          const char* Ks_next, const char* Vs,
-                                          const int (&kbase)[Cfg<D, BLK>::NKS],
+__device__ __forceinline__ void pipe_step(State<D, BLK>& st, const SAcc<D, BLK>& s,
+                                          SAcc<D, BLK>& s_next, const char* Ks_next,
+                                          const char* Vs, const int (&kbase)[Cfg<D, BLK>::NKS],
                                           const int (&vbase)[Cfg<D, BLK>::NOT],
                                           const bf16x8 (&qf)[Cfg<D, BLK>::NKS], float c, float mb) {
   using C = Cfg<D, BLK>;
-  constexpr int NSTEP = 2 * C::NKS;          // S MFMAs of one 64-key tile
-  constexpr int PER = 16 / NSTEP;            // element pairs per step (1, or 2 for d = 64)
-  static_assert(PER * NSTEP == 16, "16 element pairs (32 scores) per lane and tile");
+  constexpr int NSTEP = C::NJS * C::NKS;     // S MFMAs of one tile
+  constexpr int NPAIR = 8 * C::NJS;          // element pairs (two scores) per lane and tile
+  constexpr int PER = NPAIR / NSTEP;         // element pairs per step (1, or 2 for d = 64)
+  static_assert(PER * NSTEP == NPAIR, "pairs spread evenly over the S steps");
   constexpr int KD = 3;                      // K operand ring depth
   constexpr int VD = 4;                      // V operand ring depth
-  constexpr int NPV = 4 * C::NOT;            // PV MFMAs of one tile
-  uint32_t wd[16];
+  constexpr int NKC = 2 * C::NJS;            // 16-key PV steps of one tile
+  constexpr int NPV = NKC * C::NOT;          // PV MFMAs of one tile
+  uint32_t wd[NPAIR];
   float lsum = 0.f;
-  s_next[0] = f32x16{};
-  s_next[1] = f32x16{};
+#pragma unroll
+  for (int js = 0; js < C::NJS; ++js) s_next[js] = f32x16{};
   bf16x8 kr[KD];
 #pragma unroll
   for (int i = 0; i < KD; ++i) kr[i] = k_operand<D, BLK>(Ks_next, kbase, i);
@@ -290,11 +290,11 @@ __device__ __forceinline__ void pipe_step(State<D, BLK>& st, const f32x16 (&s)[2
     const bf16x8 ka = kr[step % KD];
     if (step + KD < NSTEP) kr[step % KD] = k_operand<D, BLK>(Ks_next, kbase, step + KD);
     const int vi = step - (NSTEP - VD);      // start the V operands in the last steps
-    if (vi >= 0) vr[vi] = v_operand<D, BLK>(Vs, vbase, vi / 4, vi % 4);
+    if (vi >= 0) vr[vi] = v_operand<D, BLK>(Vs, vbase, vi / NKC, vi % NKC);
     s_next[js] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s_next[js], 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int q = step * PER + u;          // element pair 0..15
+      const int q = step * PER + u;          // element pair
       const int ej = q >> 3, r0 = 2 * (q & 7);
       const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ej][r0], c, -mb));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(s[ej][r0 + 1], c, -mb));
@@ -308,37 +308,40 @@ __device__ __forceinline__ void pipe_step(State<D, BLK>& st, const f32x16 (&s)[2
     __builtin_amdgcn_sched_barrier(0);
   }
   st.l += lsum;
-  // pair q = 8*ej + (r0/2) holds keys of sub-tile ej, registers r0, r0+1;
-  // PV step kc = 2*ej + h2 takes registers 8*h2 .. 8*h2 + 7 of sub-tile ej
-  bf16x8 pk[4];
+  // pair q = 8*ej + (r0/2) holds keys of key group ej, registers r0, r0+1;
+  // PV step kc = 2*ej + h2 takes registers 8*h2 .. 8*h2 + 7 of key group ej
+  bf16x8 pk[NKC];
 #pragma unroll
-  for (int kc = 0; kc < 4; ++kc) {
+  for (int kc = 0; kc < NKC; ++kc) {
     const int base = 8 * (kc >> 1) + 4 * (kc & 1);
     pk[kc] = __builtin_bit_cast(bf16x8, u32x4{wd[base], wd[base + 1], wd[base + 2], wd[base + 3]});
   }
 #pragma unroll
   for (int j = 0; j < NPV; ++j) {
     const bf16x8 va = vr[j % VD];
-    if (j + VD < NPV) vr[j % VD] = v_operand<D, BLK>(Vs, vbase, (j + VD) / 4, (j + VD) % 4);
-    st.o[j / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[j % 4], st.o[j / 4], 0, 0, 0);
+    if (j + VD < NPV) vr[j % VD] = v_operand<D, BLK>(Vs, vbase, (j + VD) / NKC, (j + VD) % NKC);
+    st.o[j / NKC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[j % NKC], st.o[j / NKC], 0, 0, 0);
   }
 }
 
 template <int D, int BLK>
 __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
   using C = Cfg<D, BLK>;
-  static_assert(BLK == 128, "64-row query blocks use the 16-row-per-wave kernel");
+  using DC = DmaCfg<D, BLK>;
+  constexpr int T = C::T;
   // Double-buffered K and V tiles: tile e uses buffers K[e & 1], V[e & 1].
   // Four separate LDS objects, each named statically in every unrolled tile
   // step: the compiler can then tell that the transposed V reads of one
   // buffer do not overlap the tile loads in flight into the other, and does
   // not make the reads wait for those loads.
-  __shared__ __attribute__((aligned(1024))) char K0[KT * D * 2];
-  __shared__ __attribute__((aligned(1024))) char K1[KT * D * 2];
-  __shared__ __attribute__((aligned(1024))) char V0[KT * D * 2];
-  __shared__ __attribute__((aligned(1024))) char V1[KT * D * 2];
-  // one spare word: the tail mask reads the word after the tile's first
-  __shared__ uint32_t selbits[kMaxBlocks / 32 + 1];
+  __shared__ __attribute__((aligned(1024))) char K0[C::TB];
+  __shared__ __attribute__((aligned(1024))) char K1[C::TB];
+  __shared__ __attribute__((aligned(1024))) char V0[C::TB];
+  __shared__ __attribute__((aligned(1024))) char V1[C::TB];
+  // tail only: selection bitmap, then the ascending list of the eligible
+  // blocks that are not listed (the pooled rows the tail tiles gather)
+  __shared__ uint32_t selbits[kMaxBlocks / 32];
+  __shared__ uint16_t tail_rows[kMaxBlocks];
 
   const int item = xcd_local_item(blockIdx.x, a.total);
   if (item < 0) return;
@@ -376,20 +379,49 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
   const int n_sel = scalar_view(a.cnt)[(size_t)bh * a.M + I];
   const const_i32* list = scalar_view(a.idx + ((size_t)bh * a.M + I) * a.M);
   const int Jend = a.causal ? I + 1 : a.M;
-  const int n_exact = n_sel * C::SUB;
-  const int n_tiles = n_exact + (a.approx ? (Jend + KT - 1) / KT : 0);
   const int last_n = a.N - (a.M - 1) * BLK;
-  // tail logit offsets: log2(n_J) / (scale * log2 e)
-  const float bias_blk = __log2f((float)BLK) / a.scale_log2;
-  const float bias_last = __log2f((float)last_n) / a.scale_log2;
+  // every listed block is eligible, so Jend - n_sel eligible blocks remain
+  const int n_rest = a.approx ? Jend - n_sel : 0;
+  const int n_tt = (n_rest + T - 1) / T;   // tail tiles
+  // Only the ragged last block (J = M-1) and the causal diagonal (J = I)
+  // need the edge mask; either is the largest index a list may hold, so in
+  // an ascending list it can only be the last entry.
+  int has_edge = 0;
+  if (n_sel > 0) {
+    const int J = list[n_sel - 1];
+    has_edge = ((J + 1) * BLK > a.N || (a.causal && J >= I)) ? 1 : 0;
+  }
+  // tile order: [exact, unmasked) [tail but the last) [edge block) [last tail)
+  const int P1 = 2 * (n_sel - has_edge);
+  const int P2 = P1 + (n_tt > 0 ? n_tt - 1 : 0);
+  const int P3 = P2 + 2 * has_edge;
+  const int n_tiles = P3 + (n_tt > 0 ? 1 : 0);
+  // tail logits carry log2(n_J): log2(BLK) for every block but a short last
+  // one, whose row (the largest index, so the last tail row) gets the
+  // difference added to its score
+  const float log2_blk = __log2f((float)BLK);
+  const float last_fix = (__log2f((float)last_n) - log2_blk) / a.scale_log2;
 
   if (a.approx) {
-    for (int i = t; i < kMaxBlocks / 32 + 1; i += C::NT) selbits[i] = 0u;
+    for (int i = t; i < kMaxBlocks / 32; i += C::NT) selbits[i] = 0u;
     __syncthreads();
     for (int e = t; e < n_sel; e += C::NT) {
       const int J = list[e];
       atomicOr(&selbits[J >> 5], 1u << (J & 31));
     }
+    __syncthreads();
+    if (w == 0) {   // ballot compaction of the unlisted eligible blocks
+      int base = 0;
+      for (int J0 = 0; J0 < Jend; J0 += 64) {
+        const int J = J0 + lane;
+        const int Jc = J < Jend ? J : 0;   // keeps the bitmap read in range
+        const bool rest_J = J < Jend && !((selbits[Jc >> 5] >> (Jc & 31)) & 1u);
+        const uint64_t bal = __ballot(rest_J);
+        if (rest_J) tail_rows[base + lanes_below(bal)] = (uint16_t)J;
+        base += __popcll(bal);
+      }
+    }
+    __syncthreads();
   }
 
   const int head_bytes = a.N * C::ROWB;
@@ -414,25 +446,59 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
       vbase[nt] = jr * C::ROWB + v_chunk<D>(jr, n >> 3) * 16 + (n & 7) * 2;
     }
   }
-
-  // first key (token index, or pooled row for tail tiles) of tile e
-  auto tile_key0 = [&](int e) -> int {
-    if (e < n_exact) return list[e / C::SUB] * BLK + (e % C::SUB) * KT;
-    return (e - n_exact) * KT;
-  };
-  int koff[DmaCfg<D, BLK>::NVAR], voff[DmaCfg<D, BLK>::NVAR];
+  // DMA: this lane's first row and swizzled column offsets
+  const int row0 = w * C::RPK + lane / C::CPR;
+  int kcol[DC::NVAR], vcol[DC::NVAR];
 #pragma unroll
-  for (int i = 0; i < DmaCfg<D, BLK>::NVAR; ++i) {
-    koff[i] = dma_lane_off<D, BLK, false>(i, w, lane);
-    voff[i] = dma_lane_off<D, BLK, true>(i, w, lane);
+  for (int i = 0; i < DC::NVAR; ++i) {
+    kcol[i] = dma_col<D, BLK, false>(i, w, lane);
+    vcol[i] = dma_col<D, BLK, true>(i, w, lane);
   }
-  // exact tiles: KT keys of the head; tail tiles: KT pooled rows (bf16 block
-  // means of k and of v from the pool pass), both straight into LDS
-  auto issue_k = [&](int e, int key0, char* dst) {
-    dma_tile<D, BLK>(e < n_exact ? krs : tkrs, key0 * C::ROWB, dst, w, koff);
+
+  // Tile e: a tail tile (returns true, key = tail tile index) or an exact one
+  // (key = first token).
+  auto tile_src = [&](int e, int& key) -> bool {
+    if (e < P1) {
+      key = list[e >> 1] * BLK + (e & 1) * T;
+      return false;
+    }
+    if (e < P2) {
+      key = e - P1;
+      return true;
+    }
+    if (e < P3) {
+      key = list[n_sel - 1] * BLK + ((e - P2) & 1) * T;
+      return false;
+    }
+    key = n_tt - 1;
+    return true;
   };
-  auto issue_v = [&](int e, int key0, char* dst) {
-    dma_tile<D, BLK>(e < n_exact ? vrs : tvrs, key0 * C::ROWB, dst, w, voff);
+  // byte offsets of the pooled rows this lane copies for tail tile tt (row 0
+  // for the padding of the last tile, masked later)
+  auto tail_offs = [&](int tt, int (&ro)[C::NI]) {
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i) {
+      const int r = T * tt + row0 + i * C::NW * C::RPK;
+      ro[i] = (r < n_rest ? (int)tail_rows[r] : 0) * C::ROWB;
+    }
+  };
+  auto issue_k = [&](bool tail, int key, char* dst) {
+    if (!tail) {
+      dma_tile<D, BLK>(krs, key * C::ROWB, dst, w, row0, kcol);
+    } else {
+      int ro[C::NI];
+      tail_offs(key, ro);
+      dma_rows<D, BLK>(tkrs, ro, dst, w, kcol);
+    }
+  };
+  auto issue_v = [&](bool tail, int key, char* dst) {
+    if (!tail) {
+      dma_tile<D, BLK>(vrs, key * C::ROWB, dst, w, row0, vcol);
+    } else {
+      int ro[C::NI];
+      tail_offs(key, ro);
+      dma_rows<D, BLK>(tvrs, ro, dst, w, vcol);
+    }
   };
 
   State<D, BLK> st;
@@ -442,56 +508,75 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
   st.l = 0.f;
   const float c = a.scale_log2;
 
-  // mask tile e in place (tail tiles: selection bits, eligibility and the
-  // multiplicity offset; exact tiles: end of sequence and causal diagonal)
-  auto mask_tile = [&](f32x16 (&sv)[2], int e, int key0) {
-    if (e >= n_exact) {
-      const uint32_t w0 = selbits[key0 >> 5] >> (4 * hh);
-      const uint32_t w1 = selbits[(key0 >> 5) + 1] >> (4 * hh);
-      mask_tail(sv, Jend - key0 - 4 * hh, w0, w1, a.M - 1 - key0 - 4 * hh, bias_blk, bias_last);
-    } else if (key0 + KT > a.N || (a.causal && key0 + KT > I * BLK)) {
-      int lim = a.N - key0;
-      if (a.causal) lim = min(lim, q_tok - key0 + 1);
-      mask_exact(sv, lim - 4 * hh);
+  // masks of the last tiles, in place: the edge block (end of sequence,
+  // causal diagonal) or the last tail tile (padding rows, a short last
+  // block's multiplicity)
+  auto mask_tile = [&](f32x16 (&sv)[C::NJS], bool tail, int key) {
+    if (tail) {
+      const int lim = n_rest - T * key - 4 * hh;
+      const int fix_kr = (last_n != BLK && tail_rows[n_rest - 1] == a.M - 1) ? lim - 1 : -1;
+#pragma unroll
+      for (int js = 0; js < C::NJS; ++js)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kr = kr_of(js, r);
+          sv[js][r] = kr < lim ? (kr == fix_kr ? sv[js][r] + last_fix : sv[js][r]) : -INFINITY;
+        }
+    } else {
+      int lim = a.N - key;
+      if (a.causal) lim = min(lim, q_tok - key + 1);
+      lim -= 4 * hh;
+#pragma unroll
+      for (int js = 0; js < C::NJS; ++js)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[js][r] = kr_of(js, r) < lim ? sv[js][r] : -INFINITY;
     }
   };
 
   // Pipeline: while the softmax of tile e runs on the vector ALUs, the
   // matrix cores compute S of tile e+1; K e+2 and V e+1 load meanwhile.
   // One barrier per tile: it retires tile e's buffers and publishes the
-  // loads issued during it.
-  int key0 = tile_key0(0);
-  int key1 = n_tiles > 1 ? tile_key0(1) : 0;
-  issue_k(0, key0, K0);
-  issue_v(0, key0, V0);
-  if (n_tiles > 1) issue_k(1, key1, K1);
+  // loads issued during it.  (t0, k0): tile e; (t1, k1): tile e+1.
+  int k0 = 0, k1 = 0;
+  bool t0 = n_tiles > 0 ? tile_src(0, k0) : false;
+  bool t1 = n_tiles > 1 ? tile_src(1, k1) : false;
+  if (n_tiles > 0) {
+    issue_k(t0, k0, K0);
+    issue_v(t0, k0, V0);
+  }
+  if (n_tiles > 1) issue_k(t1, k1, K1);
   wait_vm();
   __syncthreads();
-  f32x16 s[2];
-  qk_tile<D, BLK>(s, K0, kbase, qf);
+  f32x16 sA[C::NJS], sB[C::NJS];
+  qk_tile<D, BLK>(sA, K0, kbase, qf);
 
   // one tile step; Kn holds tile e+1 (read now) and receives tile e+2, Vc
-  // holds tile e, Vn receives tile e+1
-  auto step = [&](int e, const char* Kn, char* Kc, const char* Vc, char* Vn) __attribute__((always_inline)) {
-    const int key2 = e + 2 < n_tiles ? tile_key0(e + 2) : 0;
-    if (e + 1 < n_tiles) issue_v(e + 1, key1, Vn);
-    if (e + 2 < n_tiles) issue_k(e + 2, key2, Kc);
-    mask_tile(s, e, key0);
-    const float mb = softmax_max<D, BLK>(st, s, c);
+  // holds tile e, Vn receives tile e+1; sc is S of tile e, sn receives S of
+  // tile e+1
+  auto step = [&](int e, const char* Kn, char* Kc, const char* Vc, char* Vn, f32x16 (&sc)[C::NJS],
+                  f32x16 (&sn)[C::NJS]) __attribute__((always_inline)) {
+    int k2 = 0;
+    const bool t2 = e + 2 < n_tiles ? tile_src(e + 2, k2) : false;
+    if (e + 1 < n_tiles) issue_v(t1, k1, Vn);
+    if (e + 2 < n_tiles) issue_k(t2, k2, Kc);
+    if (e >= P2) mask_tile(sc, t0, k0);   // the last tiles only
+    const float mb = softmax_max<D, BLK>(st, sc, c, t0 ? log2_blk : 0.f);
     // S of tile e+1 (on the last tile this reads a retired buffer and the
     // result is dropped) interleaved with the softmax of tile e
-    f32x16 s_next[2];
-    pipe_step<D, BLK>(st, s, s_next, Kn, Vc, kbase, vbase, qf, c, mb);
+    pipe_step<D, BLK>(st, sc, sn, Kn, Vc, kbase, vbase, qf, c, mb);
     wait_vm();
     __syncthreads();
-#pragma unroll
-    for (int js = 0; js < 2; ++js) s[js] = s_next[js];
-    key0 = key1;
-    key1 = key2;
+    t0 = t1;
+    k0 = k1;
+    t1 = t2;
+    k1 = k2;
   };
-  for (int e = 0; e < n_tiles; e += 2) {
-    step(e, K1, K0, V0, V1);
-    if (e + 1 < n_tiles) step(e + 1, K0, K1, V1, V0);
+  int e = 0;
+  while (e < n_tiles) {
+    step(e, K1, K0, V0, V1, sA, sB);
+    if (++e >= n_tiles) break;
+    step(e, K0, K1, V1, V0, sB, sA);
+    ++e;
   }
 
   // ---- epilogue: O / l, bf16, row q_tok; register r of d-tile nt holds

@@ -88,6 +88,19 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int tile_off
                                              tile_off + i * C::NW * 1024, 0, 0);
 }
 
+// Gather: like dma_tile, but instruction i reads this lane's chunk of the
+// row at byte offset ro[i] (per-lane rows, e.g. the pooled rows of a tail
+// tile).
+template <int D, int BLK>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, const int (&ro)[Cfg<D, BLK>::NI], int col,
+                                         char* lds, int w) {
+  using C = Cfg<D, BLK>;
+#pragma unroll
+  for (int i = 0; i < C::NI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (i * C::NW + w) * 1024), 16, ro[i] + col, 0, 0,
+                                             0);
+}
+
 // value of a query row over its four lanes (l%16 + 16g)
 __device__ __forceinline__ float row_max4(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -109,8 +122,10 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
   constexpr int TB = KT * D * 2;   // bytes of one K or V tile
   __shared__ __attribute__((aligned(1024))) char Ks[TB];
   __shared__ __attribute__((aligned(1024))) char Vs[TB];
-  // one spare word: the tail mask reads the word after the tile's first
-  __shared__ uint32_t selbits[kMaxBlocks / 32 + 1];
+  // tail only: selection bitmap, then the ascending list of the eligible
+  // blocks that are not listed (the pooled rows the tail tiles gather)
+  __shared__ uint32_t selbits[kMaxBlocks / 32];
+  __shared__ uint16_t tail_rows[kMaxBlocks];
 
   const int item = xcd_local_item(blockIdx.x, a.total);
   if (item < 0) return;
@@ -147,18 +162,36 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
   const const_i32* list = scalar_view(a.idx + ((size_t)bh * a.M + I) * a.M);
   const int Jend = a.causal ? I + 1 : a.M;
   const int n_exact = n_sel;
-  const int n_tiles = n_exact + (a.approx ? (Jend + KT - 1) / KT : 0);
+  // every listed block is eligible, so Jend - n_sel eligible blocks remain
+  const int n_rest = a.approx ? Jend - n_sel : 0;
+  const int n_tiles = n_exact + (n_rest + KT - 1) / KT;
   const int last_n = a.N - (a.M - 1) * BLK;
-  const float bias_blk = __log2f((float)BLK) / a.scale_log2;
-  const float bias_last = __log2f((float)last_n) / a.scale_log2;
+  // tail logits carry log2(n_J): log2(BLK) for every block but a short last
+  // one, whose row (the largest index, so the last tail row) gets the
+  // difference added to its score
+  const float log2_blk = __log2f((float)BLK);
+  const float last_fix = (__log2f((float)last_n) - log2_blk) / a.scale_log2;
 
   if (a.approx) {
-    for (int i = t; i < kMaxBlocks / 32 + 1; i += C::NT) selbits[i] = 0u;
+    for (int i = t; i < kMaxBlocks / 32; i += C::NT) selbits[i] = 0u;
     __syncthreads();
     for (int e = t; e < n_sel; e += C::NT) {
       const int J = list[e];
       atomicOr(&selbits[J >> 5], 1u << (J & 31));
     }
+    __syncthreads();
+    if (w == 0) {   // ballot compaction of the unlisted eligible blocks
+      int base = 0;
+      for (int J0 = 0; J0 < Jend; J0 += 64) {
+        const int J = J0 + lane;
+        const int Jc = J < Jend ? J : 0;   // keeps the bitmap read in range
+        const bool rest_J = J < Jend && !((selbits[Jc >> 5] >> (Jc & 31)) & 1u);
+        const uint64_t bal = __ballot(rest_J);
+        if (rest_J) tail_rows[base + lanes_below(bal)] = (uint16_t)J;
+        base += __popcll(bal);
+      }
+    }
+    __syncthreads();
   }
 
   const int head_bytes = a.N * C::ROWB;
@@ -169,6 +202,11 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
   const __amdgpu_buffer_rsrc_t tvrs = head_rsrc(a.approx ? a.tail_v + pp_off : a.v, a.M * C::ROWB);
   const int koff = dma_lane_off<D, BLK, false>(w, lane);
   const int voff = dma_lane_off<D, BLK, true>(w, lane);
+  // tail gathers: the row this lane copies with DMA instruction i of a tile
+  // is row0 + i * NW * RPK; its chunk offset inside the row is fixed
+  const int row0 = (w * 64 + lane) / C::CPR;
+  const int kcol = koff - row0 * C::ROWB;
+  const int vcol = voff - row0 * C::ROWB;
 
   // LDS operand addresses (tile-invariant): K rows 16t + lr, chunk 4s + lg;
   // V transpose-read source rows 4*lg + (lr >> 2) (+32c, +16 half), columns
@@ -186,14 +224,35 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
     }
   }
 
-  // first key (token, or pooled row for tail tiles) of tile e; one 64-key
-  // tile per listed block
-  auto tile_key0 = [&](int e) -> int { return e < n_exact ? list[e] * BLK : (e - n_exact) * KT; };
+  // first key of exact tile e (one 64-key tile per listed block); tail
+  // tiles are numbered from 0 and gather KT pooled rows each
+  auto tile_key0 = [&](int e) -> int { return e < n_exact ? list[e] * BLK : e - n_exact; };
+  // tail tile tt: byte offsets (row index from tail_rows, 0 for the padding
+  // of the last tile, masked later) of this lane's rows
+  auto tail_offs = [&](int tt, int (&ro)[C::NI]) {
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i) {
+      const int r = KT * tt + row0 + i * C::NW * C::RPK;
+      ro[i] = (r < n_rest ? (int)tail_rows[r] : 0) * C::ROWB;
+    }
+  };
   auto issue_k = [&](int e, int key0) {
-    dma_tile<D, BLK>(e < n_exact ? krs : tkrs, key0 * C::ROWB, Ks, w, koff);
+    if (e < n_exact) {
+      dma_tile<D, BLK>(krs, key0 * C::ROWB, Ks, w, koff);
+    } else {
+      int ro[C::NI];
+      tail_offs(key0, ro);
+      dma_rows<D, BLK>(tkrs, ro, kcol, Ks, w);
+    }
   };
   auto issue_v = [&](int e, int key0) {
-    dma_tile<D, BLK>(e < n_exact ? vrs : tvrs, key0 * C::ROWB, Vs, w, voff);
+    if (e < n_exact) {
+      dma_tile<D, BLK>(vrs, key0 * C::ROWB, Vs, w, voff);
+    } else {
+      int ro[C::NI];
+      tail_offs(key0, ro);
+      dma_rows<D, BLK>(tvrs, ro, vcol, Vs, w);
+    }
   };
 
   f32x4 o[C::NOT];
@@ -238,21 +297,18 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
     if (e + 1 < n_tiles) issue_k(e + 1, key1);
 
     // ---- masks: register r of key group tg holds key key0 + 16*tg + 4*lg + r
-    if constexpr (MODE == kModeTail) {
-      const int lim = Jend - key0 - 4 * lg;
-      const int last_kr = a.M - 1 - key0 - 4 * lg;
-      const uint32_t w0 = selbits[key0 >> 5] >> (4 * lg);
-      const uint32_t w1 = selbits[(key0 >> 5) + 1] >> (4 * lg);
+    if constexpr (MODE == kModeTailLast) {
+      // last tail tile: padding rows masked; a short last block's row (the
+      // last real row when listed here) gets its multiplicity fix
+      const int lim = n_rest - KT * key0 - 4 * lg;
+      const int fix_kr = (last_n != BLK && tail_rows[n_rest - 1] == a.M - 1) ? lim - 1 : -1;
 #pragma unroll
-      for (int tg = 0; tg < 4; ++tg) {
-        const uint32_t word = tg < 2 ? w0 : w1;
+      for (int tg = 0; tg < 4; ++tg)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int kr = 16 * tg + r;            // key - key0 - 4*lg
-          const bool on = kr < lim && !((word >> (kr & 31)) & 1u);
-          s[tg][r] = on ? s[tg][r] + (kr == last_kr ? bias_last : bias_blk) : -INFINITY;
+          const int kr = 16 * tg + r;            // row - KT*tt - 4*lg
+          s[tg][r] = kr < lim ? (kr == fix_kr ? s[tg][r] + last_fix : s[tg][r]) : -INFINITY;
         }
-      }
     } else if constexpr (MODE == kModeEdge) {
       int lim = a.N - key0;
       if (a.causal) lim = min(lim, q_tok - key0 + 1);
@@ -270,7 +326,10 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[tg][r]);
     mx = row_max4(mx);
-    const float mxs = mx * c;
+    // tail rows: + log2(n_J) (a uniform offset; a short last block's
+    // difference is already in its score)
+    const float lb = MODE >= kModeTail ? log2_blk : 0.f;
+    const float mxs = fmaf(mx, c, lb);
     const bool grow = mxs > m + 8.f;
     if (__ballot(grow)) {
       const float m_new = grow ? mxs : m;
@@ -280,7 +339,7 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
       for (int nt = 0; nt < C::NOT; ++nt) o[nt] *= corr;
       m = m_new;
     }
-    const float mb = m == -INFINITY ? 0.f : m;
+    const float mb = (m == -INFINITY ? 0.f : m) - lb;
     uint32_t wd[8];
     float lsum = 0.f;
 #pragma unroll
@@ -353,11 +412,12 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
     step(e, key0, key1, ModeC<kModeEdge>{});
     key0 = key1;
   }
-  for (; e < n_tiles; ++e) {
-    const int key1 = e + 1 < n_tiles ? tile_key0(e + 1) : 0;
+  for (; e < n_tiles - 1; ++e) {
+    const int key1 = tile_key0(e + 1);
     step(e, key0, key1, ModeC<kModeTail>{});
     key0 = key1;
   }
+  if (e < n_tiles) step(e, key0, 0, ModeC<kModeTailLast>{});
 
   // ---- epilogue: register r of d-tile nt holds d = 16*nt + 4*lg + r
   const float lt = row_sum4(l);

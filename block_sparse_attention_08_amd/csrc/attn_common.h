@@ -19,8 +19,9 @@ constexpr int KT = 64;  // keys per tile (a 128-token block is two tiles)
 constexpr bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 
 // Masking a tile needs: none (interior exact tile), the ragged end / causal
-// diagonal (edge), or the tail rules (pooled rows).
-enum { kModePlain = 0, kModeEdge = 1, kModeTail = 2 };
+// diagonal (edge); tail tiles of pooled rows need none but the log2(n_J)
+// offset, except the last one (padding rows, a short last block).
+enum { kModePlain = 0, kModeEdge = 1, kModeTail = 2, kModeTailLast = 3 };
 template <int MODE>
 struct ModeC { static constexpr int value = MODE; };
 
