@@ -54,6 +54,8 @@ def parse():
                    help="also run one device copy of this size (counter calibration runs)")
     p.add_argument("--dense", action="store_true",
                    help="attend every eligible block (caller lists), the dense comparison run")
+    p.add_argument("--fused-route", action="store_true",
+                   help="pool + select in one cooperative launch (sparse_attn_route)")
     return p.parse_args()
 
 
@@ -214,12 +216,18 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record()
-        bsa.block_pool(desc, qd, kd, vd, ws.q_bar, ws.k_bar, ws.v_sum, ws.tail)
-        if ev:
-            ev[1].record()
-        bsa.select(desc, ws.q_bar, ws.k_bar, ws.blk_idx, ws.blk_cnt)
-        if ev:
-            ev[2].record()
+        if args.fused_route:
+            bsa.route(desc, qd, kd, vd, ws.q_bar, ws.k_bar, ws.v_sum, ws.tail, ws.blk_idx, ws.blk_cnt)
+            if ev:
+                ev[1].record()
+                ev[2].record()
+        else:
+            bsa.block_pool(desc, qd, kd, vd, ws.q_bar, ws.k_bar, ws.v_sum, ws.tail)
+            if ev:
+                ev[1].record()
+            bsa.select(desc, ws.q_bar, ws.k_bar, ws.blk_idx, ws.blk_cnt)
+            if ev:
+                ev[2].record()
         if args.dense:
             bsa.fwd(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, dense_idx, dense_cnt, out)
         else:
@@ -290,7 +298,8 @@ def main():
                    "block": wl.block, "causal": wl.causal,
                    "selection": (f"alpha={wl.alpha}" if wl.select == "alpha"
                                  else f"density={wl.density}") if not args.dense else "all",
-                   "tail": bool(wl.approx and not args.dense), "parallelism": "single-gpu"},
+                   "tail": bool(wl.approx and not args.dense), "parallelism": "single-gpu",
+                   "routing": "fused" if args.fused_route else "pool+select"},
         "roofline": {
             "bound": "mfma",
             "kernel": ("attn_f32_kernel" if wl.dtype != "bf16" else

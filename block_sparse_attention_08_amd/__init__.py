@@ -11,7 +11,8 @@ torch supplies device memory and streams.
 
 q: [B, Hq, N, d], k/v: [B, Hkv, N, d], contiguous, bfloat16 or float32, on
 the GPU.  The three stages are also exposed one by one (``block_pool``,
-``select``, ``fwd``) with caller-owned buffers from ``Workspace``.
+``select``, ``fwd``) with caller-owned buffers from ``Workspace``; ``route``
+runs the first two in one launch.
 """
 
 from __future__ import annotations
@@ -24,7 +25,7 @@ from ._lib import SA_DTYPE_BF16, SA_DTYPE_F32, SA_SELECT_ALPHA, SA_SELECT_DENSIT
 
 __all__ = [
     "Workspace", "block_pool", "block_sparse_attention", "buffer_sizes", "fwd", "make_desc",
-    "select", "SparseAttnError", "abi_version",
+    "route", "select", "SparseAttnError", "abi_version",
 ]
 
 
@@ -106,6 +107,15 @@ def select(desc, q_bar, k_bar, blk_idx, blk_cnt, stream=None) -> None:
     st = _lib.lib().sparse_attn_select(desc, _ptr(q_bar), _ptr(k_bar), _ptr(blk_idx),
                                        _ptr(blk_cnt), _stream(stream))
     _lib.check(st, "sparse_attn_select")
+
+
+def route(desc, q, k, v, q_bar, k_bar, v_sum, tail, blk_idx, blk_cnt, stream=None) -> None:
+    """Stages 1 + 2 in one cooperative launch (fused routing): writes what
+    ``block_pool`` then ``select`` write."""
+    st = _lib.lib().sparse_attn_route(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(q_bar), _ptr(k_bar),
+                                      _ptr(v_sum), _ptr(tail), _ptr(blk_idx), _ptr(blk_cnt),
+                                      _stream(stream))
+    _lib.check(st, "sparse_attn_route")
 
 
 def fwd(desc, q, k, v, k_bar, v_sum, tail, blk_idx, blk_cnt, out, stream=None) -> None:

@@ -61,6 +61,7 @@ _SIGS = {
     "sparse_attn_buffer_sizes": [ctypes.POINTER(SaDesc), ctypes.POINTER(SaSizes)],
     "sparse_attn_block_pool": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P, _P, _P, _P],
     "sparse_attn_select": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P],
+    "sparse_attn_route": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "sparse_attn_fwd": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "sparse_attn_status_string": [ctypes.c_int],
     "sparse_attn_abi_version": [],

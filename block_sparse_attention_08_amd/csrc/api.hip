@@ -53,6 +53,17 @@ float resolve_scale(const sa_desc* d) {
 
 sa_status from_hip(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
 
+sa::SelectParams select_params(const sa_desc* d) {
+  sa::SelectParams p;
+  p.scale = resolve_scale(d);
+  p.mode = d->select_mode;
+  p.alpha = (float)d->alpha;
+  p.density = d->density;
+  p.causal = d->causal;
+  p.force_diag = d->causal && d->approx;
+  return p;
+}
+
 }  // namespace
 
 SA_EXPORT int32_t sparse_attn_abi_version(void) { return SPARSE_ATTN_ABI_VERSION; }
@@ -112,14 +123,28 @@ SA_EXPORT sa_status sparse_attn_select(const sa_desc* desc, const float* q_bar, 
   if (!q_bar || !k_bar || !blk_idx || !blk_cnt) return SA_ERR_NULL;
   if (!aligned16(q_bar) || !aligned16(k_bar) || !aligned16(blk_idx) || !aligned16(blk_cnt))
     return SA_ERR_ALIGN;
-  sa::SelectParams p;
-  p.scale = resolve_scale(desc);
-  p.mode = desc->select_mode;
-  p.alpha = (float)desc->alpha;
-  p.density = desc->density;
-  p.causal = desc->causal;
-  p.force_diag = desc->causal && desc->approx;
-  return from_hip(sa::launch_select(s, p, q_bar, k_bar, blk_idx, blk_cnt, (hipStream_t)stream));
+  return from_hip(sa::launch_select(s, select_params(desc), q_bar, k_bar, blk_idx, blk_cnt,
+                                    (hipStream_t)stream));
+}
+
+SA_EXPORT sa_status sparse_attn_route(const sa_desc* desc, const void* q, const void* k, const void* v,
+                                      float* q_bar, float* k_bar, float* v_sum, void* tail,
+                                      int32_t* blk_idx, int32_t* blk_cnt, void* stream) {
+  sa::Shape s;
+  const sa_status st = check_desc(desc, &s);
+  if (st != SA_OK) return st;
+  const bool need_tail = desc->approx && desc->dtype == SA_DTYPE_BF16;
+  if (!q || !k || !q_bar || !k_bar || !blk_idx || !blk_cnt) return SA_ERR_NULL;
+  if (desc->approx && (!v || !v_sum)) return SA_ERR_NULL;
+  if (need_tail && !tail) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_bar) || !aligned16(k_bar) || !aligned16(blk_idx) ||
+      !aligned16(blk_cnt))
+    return SA_ERR_ALIGN;
+  if (desc->approx && (!aligned16(v) || !aligned16(v_sum))) return SA_ERR_ALIGN;
+  if (need_tail && !aligned16(tail)) return SA_ERR_ALIGN;
+  return from_hip(sa::launch_route_fused(s, select_params(desc), q, k, desc->approx ? v : nullptr, q_bar,
+                                         k_bar, desc->approx ? v_sum : nullptr, need_tail ? tail : nullptr,
+                                         blk_idx, blk_cnt, (hipStream_t)stream));
 }
 
 SA_EXPORT sa_status sparse_attn_fwd(const sa_desc* desc, const void* q, const void* k, const void* v,

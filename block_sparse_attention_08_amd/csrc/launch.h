@@ -29,6 +29,12 @@ struct SelectParams {
 hipError_t launch_select(const Shape& s, const SelectParams& p, const float* q_bar,
                          const float* k_bar, int32_t* blk_idx, int32_t* blk_cnt, hipStream_t st);
 
+// Stages 1 + 2 in one cooperative launch (same outputs as launch_pool then
+// launch_select).
+hipError_t launch_route_fused(const Shape& s, const SelectParams& p, const void* q, const void* k,
+                              const void* v, float* q_bar, float* k_bar, float* v_sum, void* tail,
+                              int32_t* blk_idx, int32_t* blk_cnt, hipStream_t st);
+
 // Stage 3: attention over the listed blocks (+ 0th-order tail).
 struct FwdParams {
   float scale;

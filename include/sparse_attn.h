@@ -90,7 +90,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 2
+#define SPARSE_ATTN_ABI_VERSION 3
 
 typedef enum {
   SA_OK = 0,
@@ -145,6 +145,19 @@ sa_status sparse_attn_block_pool(const sa_desc* desc, const void* q, const void*
  * every row into blk_idx / blk_cnt. */
 sa_status sparse_attn_select(const sa_desc* desc, const float* q_bar, const float* k_bar,
                              int32_t* blk_idx, int32_t* blk_cnt, void* stream);
+
+/* Stages 1 + 2 in one launch ("fused routing": FlashPrefill summary 2(a),
+ * pattern discovery from pooled blocks, and 2(b)-(c), threshold and index
+ * lists, without a second launch).  Writes exactly what
+ * sparse_attn_block_pool followed by sparse_attn_select writes (same
+ * buffers, same values, same arguments and errors as the two calls).  The
+ * kernel is launched cooperatively (all its workgroups resident at once, one
+ * grid-wide barrier between pooling and scoring); SA_ERR_HIP if the device
+ * refuses the cooperative launch.  On MI355X the two separate calls are the
+ * faster path: the barrier costs more than the launch it saves. */
+sa_status sparse_attn_route(const sa_desc* desc, const void* q, const void* k, const void* v,
+                            float* q_bar, float* k_bar, float* v_sum, void* tail, int32_t* blk_idx,
+                            int32_t* blk_cnt, void* stream);
 
 /* Stage 3, attention: exact online-softmax attention over the listed blocks
  * (+ the 0th-order tail over unlisted eligible blocks when approx == 1),

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
     h = _lib.lib()
     for name in _declared():
         assert hasattr(h, name), name
-    assert bsa.abi_version() == 2
+    assert bsa.abi_version() == 3
 
 
 @pytest.mark.skipif(not os.path.exists(_lib.PEAKS_PATH), reason="libsa_peaks.so not built")
@@ -138,9 +138,11 @@ def test_compute_calls_reject_null_pointers_before_launch():
     assert h.sparse_attn_select(d, None, None, None, None, None) == 1
     assert h.sparse_attn_fwd(d, None, None, None, None, None, None, None, None, None, None) == 1
     assert h.sparse_attn_buffer_sizes(None, None) == 1
+    assert h.sparse_attn_route(d, None, None, None, None, None, None, None, None, None, None) == 1
     # misaligned (never dereferenced: validation returns first)
     bad = ctypes.c_void_p(0x1003)
     assert h.sparse_attn_select(d, bad, bad, bad, bad, None) == 5
+    assert h.sparse_attn_route(d, bad, bad, bad, bad, bad, bad, bad, bad, bad, None) == 5
 
 
 def test_make_desc_needs_exactly_one_rule():
