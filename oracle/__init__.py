@@ -30,11 +30,17 @@ Pin status (what ties each function to something other than itself):
 * attention with the 0th-order tail: pinned (density 1 equals dense softmax
   attention from a library routine; identical keys inside every block make the
   tail exact; online recurrence equals the closed form; hand-derived closed-form
-  cases; brute force).
+  cases; brute force);
+* gradients of the attention step (``backward``): pinned by central finite
+  differences of the forward on small inputs (exact keys and the tail, causal,
+  grouped queries, ragged blocks) and, for density 1, by torch's autograd of
+  dense softmax attention.
 """
 
 from .reference import (  # noqa: F401
     attend_block,
+    attend_block_grad,
+    backward,
     band_mask,
     block_bounds,
     block_scores,

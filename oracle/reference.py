@@ -297,3 +297,105 @@ def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, block: int, causal: 
             mask[b, h, I], elig[I], block=block, scale=scale, causal=causal, approx=approx)
     return dict(q_bar=q_bar, k_bar=k_bar, v_sum=v_sum, n=block_sizes(N, block), scores=s,
                 mask=mask, thresholds=t, out=out)
+
+
+# --------------------------------------------------------------------------
+# gradients of the attention step (the training path of the 0th-order form)
+#   PISA explainer, "minimal documented usage": the simplified 0th-order
+#   variant is the one meant for training, so gradients flow through the
+#   exact blocks and through the pooled pseudo-keys of the tail.  The block
+#   selection is piecewise constant in the inputs and passes no gradient;
+#   the selection mask is an input here.
+#
+#   With P_ia the softmax weight of key a (exact token j: exp(z_ij)/den;
+#   pooled block J: n_J exp(z_iJ)/den) and u_a its value (v_j, or the block
+#   mean SigmaV_J / n_J), o_i = sum_a P_ia u_a and, for a loss with gradient
+#   dO at o:
+#     dz_ia = P_ia (dO_i . u_a - dO_i . o_i)
+#     dq_i  = scale sum_a dz_ia key_a            (key: k_j or kbar_J)
+#     dk_j += scale dz_ij q_i,  dv_j += P_ij dO_i            (exact keys)
+#     dkbar_J = scale sum_i dz_iJ q_i, du_J = sum_i P_iJ dO_i  (pooled)
+#   and the block means hand dkbar_J / n_J and du_J / n_J to every token of
+#   block J.
+# --------------------------------------------------------------------------
+
+def attend_block_grad(q_rows: np.ndarray, row0: int, dout_rows: np.ndarray, k: np.ndarray,
+                      v: np.ndarray, sel_row: np.ndarray, elig_row: np.ndarray, *, block: int,
+                      scale: float, causal: bool, approx: bool):
+    """Gradients from one (batch, head, query block): returns (dq_rows
+    [nI, d], dk [N, d], dv [N, d]) with dk, dv of the KV head (exact keys
+    and the tokens under each pooled block), float64."""
+    N, d = k.shape
+    nI = q_rows.shape[0]
+    qf = np.asarray(q_rows, dtype=np.float64)
+    go = np.asarray(dout_rows, dtype=np.float64)
+    kf = np.asarray(k, dtype=np.float64)
+    vf = np.asarray(v, dtype=np.float64)
+    bounds = block_bounds(N, block)
+    S = [J for J in range(len(bounds)) if sel_row[J]]
+    keys = np.concatenate([np.arange(*bounds[J]) for J in S]) if S else np.zeros(0, int)
+    T = [J for J in range(len(bounds)) if approx and elig_row[J] and not sel_row[J]]
+    n = np.array([bounds[J][1] - bounds[J][0] for J in T], dtype=np.float64)
+    kbar = np.stack([kf[slice(*bounds[J])].mean(axis=0) for J in T]) if T else np.zeros((0, d))
+    ubar = np.stack([vf[slice(*bounds[J])].mean(axis=0) for J in T]) if T else np.zeros((0, d))
+
+    z = scale * (qf @ kf[keys].T)
+    if causal:
+        tok = row0 + np.arange(nI)
+        z = np.where(keys[None, :] <= tok[:, None], z, -np.inf)
+    zt = scale * (qf @ kbar.T) + np.log(n)[None, :] if T else np.zeros((nI, 0))
+    m = np.maximum(z.max(axis=1, initial=-np.inf), zt.max(axis=1, initial=-np.inf))
+    m = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(z - m[:, None])
+    et = np.exp(zt - m[:, None])
+    den = e.sum(axis=1) + et.sum(axis=1)
+    den = np.where(den > 0, den, 1.0)
+    P = e / den[:, None]                  # exact weights
+    Pt = et / den[:, None]                # pooled weights (multiplicity included)
+    o = P @ vf[keys] + Pt @ ubar
+    Dlt = (go * o).sum(axis=1)
+    dz = P * (go @ vf[keys].T - Dlt[:, None])
+    dzt = Pt * (go @ ubar.T - Dlt[:, None])
+
+    dq = scale * (dz @ kf[keys] + dzt @ kbar)
+    dk = np.zeros((N, d))
+    dv = np.zeros((N, d))
+    np.add.at(dk, keys, scale * (dz.T @ qf))
+    np.add.at(dv, keys, P.T @ go)
+    dkbar = scale * (dzt.T @ qf)
+    dubar = Pt.T @ go
+    for t, J in enumerate(T):
+        s0, s1 = bounds[J]
+        dk[s0:s1] += dkbar[t] / n[t]
+        dv[s0:s1] += dubar[t] / n[t]
+    return dq, dk, dv
+
+
+def backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, sel: np.ndarray, *,
+             block: int, causal: bool, approx: bool,
+             scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Gradients (dq [B,Hq,N,d], dk, dv [B,Hkv,N,d], float64) of
+    sum(dout * forward(...)["out"]) for the fixed selection mask ``sel``
+    [B,Hq,M,M].  Query heads of one KV group add into its dk, dv."""
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    M = -(-N // block)
+    elig = eligible_mask(M, causal)
+    bounds = block_bounds(N, block)
+    dq = np.zeros((B, Hq, N, d))
+    dk = np.zeros((B, Hkv, N, d))
+    dv = np.zeros((B, Hkv, N, d))
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_group(h, Hq, Hkv)
+            for I in range(M):
+                r0, r1 = bounds[I]
+                gq, gk, gv = attend_block_grad(q[b, h, r0:r1], r0, dout[b, h, r0:r1], k[b, g], v[b, g],
+                                               sel[b, h, I], elig[I], block=block, scale=scale,
+                                               causal=causal, approx=approx)
+                dq[b, h, r0:r1] = gq
+                dk[b, g] += gk
+                dv[b, g] += gv
+    return dict(dq=dq, dk=dk, dv=dv)
