@@ -25,7 +25,8 @@ from ._lib import SA_DTYPE_BF16, SA_DTYPE_F32, SA_SELECT_ALPHA, SA_SELECT_DENSIT
 
 __all__ = [
     "Workspace", "block_pool", "block_sparse_attention", "buffer_sizes", "fwd", "make_desc",
-    "route", "select", "SparseAttnError", "abi_version",
+    "route", "select", "SparseAttnError", "abi_version", "fwd_lse", "bwd_buffer_sizes",
+    "BwdWorkspace", "bwd",
 ]
 
 
@@ -125,6 +126,54 @@ def fwd(desc, q, k, v, k_bar, v_sum, tail, blk_idx, blk_cnt, out, stream=None) -
                                     _ptr(tail), _ptr(blk_idx), _ptr(blk_cnt), _ptr(out),
                                     _stream(stream))
     _lib.check(st, "sparse_attn_fwd")
+
+
+def fwd_lse(desc, q, k, v, k_bar, v_sum, tail, blk_idx, blk_cnt, out, lse, stream=None) -> None:
+    """Stage 3 that also writes ``lse`` [B, Hq, N] float32 (log of each row's
+    softmax denominator), for the backward."""
+    st = _lib.lib().sparse_attn_fwd_lse(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(k_bar), _ptr(v_sum),
+                                        _ptr(tail), _ptr(blk_idx), _ptr(blk_cnt), _ptr(out), _ptr(lse),
+                                        _stream(stream))
+    _lib.check(st, "sparse_attn_fwd_lse")
+
+
+def bwd_buffer_sizes(desc: SaDesc) -> dict:
+    """Bytes of each backward buffer (host-only call)."""
+    s = _lib.SaBwdSizes()
+    _lib.check(_lib.lib().sparse_attn_bwd_buffer_sizes(desc, s), "sparse_attn_bwd_buffer_sizes")
+    return {n: int(getattr(s, n)) for n, _ in s._fields_}
+
+
+class BwdWorkspace:
+    """Caller-owned buffers of the backward: lse (from ``fwd_lse``) and the
+    scratch of ``bwd``."""
+
+    def __init__(self, desc: SaDesc, device="cuda"):
+        import torch
+        sz = bwd_buffer_sizes(desc)
+        B, Hq, Hkv, N, d, M = desc.batch, desc.heads_q, desc.heads_kv, desc.seq_len, desc.head_dim, _m(desc)
+        f32, i32 = torch.float32, torch.int32
+        W = -(-M // 32)
+        self.lse = torch.empty((B, Hq, N), dtype=f32, device=device)
+        self.delta = torch.empty((B, Hq, N), dtype=f32, device=device)
+        self.sel_bits = torch.empty((B, Hq, M, W), dtype=i32, device=device)
+        self.col_idx = torch.empty(sz["col_idx"] // 4, dtype=i32, device=device)
+        self.col_cnt = torch.empty((B, Hkv, M), dtype=i32, device=device)
+        self.dk_bar = torch.empty((B, Hkv, M, d), dtype=f32, device=device) if sz["dk_bar"] else None
+        self.dv_bar = torch.empty((B, Hkv, M, d), dtype=f32, device=device) if sz["dv_bar"] else None
+        assert self.sel_bits.numel() * 4 == sz["sel_bits"] and self.lse.numel() * 4 == sz["lse"]
+
+
+def bwd(desc, q, k, v, tail, blk_idx, blk_cnt, out, dout, bws: BwdWorkspace, dq, dk, dv,
+        stream=None) -> None:
+    """Gradients dq, dk, dv (bf16) of sum(dout * out) for the lists the
+    forward used; ``out`` and ``bws.lse`` come from ``fwd_lse``."""
+    st = _lib.lib().sparse_attn_bwd(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(tail), _ptr(blk_idx),
+                                    _ptr(blk_cnt), _ptr(out), _ptr(bws.lse), _ptr(dout), _ptr(bws.delta),
+                                    _ptr(bws.sel_bits), _ptr(bws.col_idx), _ptr(bws.col_cnt),
+                                    _ptr(bws.dk_bar), _ptr(bws.dv_bar), _ptr(dq), _ptr(dk), _ptr(dv),
+                                    _stream(stream))
+    _lib.check(st, "sparse_attn_bwd")
 
 
 def _check_tensors(q, k, v):

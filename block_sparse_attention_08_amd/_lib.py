@@ -46,6 +46,11 @@ class SaSizes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("q_bar", "k_bar", "v_sum", "tail", "blk_idx", "blk_cnt")]
 
 
+class SaBwdSizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("lse", "delta", "sel_bits", "col_idx", "col_cnt", "dk_bar",
+                                               "dv_bar")]
+
+
 class SparseAttnError(ValueError):
     def __init__(self, status: int, what: str, text: str):
         super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({text})")
@@ -62,6 +67,9 @@ _SIGS = {
     "sparse_attn_block_pool": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P, _P, _P, _P],
     "sparse_attn_select": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P],
     "sparse_attn_route": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "sparse_attn_fwd_lse": [ctypes.POINTER(SaDesc)] + [_P] * 11,
+    "sparse_attn_bwd_buffer_sizes": [ctypes.POINTER(SaDesc), ctypes.POINTER(SaBwdSizes)],
+    "sparse_attn_bwd": [ctypes.POINTER(SaDesc)] + [_P] * 19,
     "sparse_attn_fwd": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "sparse_attn_status_string": [ctypes.c_int],
     "sparse_attn_abi_version": [],

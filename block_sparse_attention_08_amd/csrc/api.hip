@@ -147,10 +147,11 @@ SA_EXPORT sa_status sparse_attn_route(const sa_desc* desc, const void* q, const 
                                          blk_idx, blk_cnt, (hipStream_t)stream));
 }
 
-SA_EXPORT sa_status sparse_attn_fwd(const sa_desc* desc, const void* q, const void* k, const void* v,
-                                    const float* k_bar, const float* v_sum, const void* tail,
-                                    const int32_t* blk_idx, const int32_t* blk_cnt, void* out,
-                                    void* stream) {
+namespace {
+
+sa_status fwd_impl(const sa_desc* desc, const void* q, const void* k, const void* v, const float* k_bar,
+                   const float* v_sum, const void* tail, const int32_t* blk_idx, const int32_t* blk_cnt,
+                   void* out, float* lse, void* stream) {
   sa::Shape s;
   const sa_status st = check_desc(desc, &s);
   if (st != SA_OK) return st;
@@ -164,11 +165,90 @@ SA_EXPORT sa_status sparse_attn_fwd(const sa_desc* desc, const void* q, const vo
     return SA_ERR_ALIGN;
   if (f32_tail && (!aligned16(k_bar) || !aligned16(v_sum))) return SA_ERR_ALIGN;
   if (bf16_tail && !aligned16(tail)) return SA_ERR_ALIGN;
+  if (lse && !aligned16(lse)) return SA_ERR_ALIGN;
   sa::FwdParams p;
   p.scale = resolve_scale(desc);
   p.causal = desc->causal;
   p.approx = desc->approx;
+  p.lse = lse;
   return from_hip(sa::launch_fwd(s, p, q, k, v, f32_tail ? k_bar : nullptr, f32_tail ? v_sum : nullptr,
                                  bf16_tail ? tail : nullptr, blk_idx, blk_cnt, out,
                                  (hipStream_t)stream));
+}
+
+}  // namespace
+
+SA_EXPORT sa_status sparse_attn_fwd(const sa_desc* desc, const void* q, const void* k, const void* v,
+                                    const float* k_bar, const float* v_sum, const void* tail,
+                                    const int32_t* blk_idx, const int32_t* blk_cnt, void* out,
+                                    void* stream) {
+  return fwd_impl(desc, q, k, v, k_bar, v_sum, tail, blk_idx, blk_cnt, out, nullptr, stream);
+}
+
+SA_EXPORT sa_status sparse_attn_bwd_buffer_sizes(const sa_desc* desc, sa_bwd_sizes* sizes) {
+  sa::Shape s;
+  const sa_status st = check_desc(desc, &s);
+  if (st != SA_OK) return st;
+  if (!sizes) return SA_ERR_NULL;
+  const sa::BwdSizes z = sa::bwd_sizes(s, desc->approx);
+  sizes->lse = z.lse;
+  sizes->delta = z.delta;
+  sizes->sel_bits = z.sel_bits;
+  sizes->col_idx = z.col_idx;
+  sizes->col_cnt = z.col_cnt;
+  sizes->dk_bar = z.dk_bar;
+  sizes->dv_bar = z.dv_bar;
+  return SA_OK;
+}
+
+SA_EXPORT sa_status sparse_attn_bwd(const sa_desc* desc, const void* q, const void* k, const void* v,
+                                    const void* tail, const int32_t* blk_idx, const int32_t* blk_cnt,
+                                    const void* out, const float* lse, const void* dout, float* delta,
+                                    uint32_t* sel_bits, int32_t* col_idx, int32_t* col_cnt, float* dk_bar,
+                                    float* dv_bar, void* dq, void* dk, void* dv, void* stream) {
+  sa::Shape s;
+  const sa_status st = check_desc(desc, &s);
+  if (st != SA_OK) return st;
+  if (desc->dtype != SA_DTYPE_BF16) return SA_ERR_UNSUPPORTED;
+  const bool ap = desc->approx != 0;
+  if (!q || !k || !v || !blk_idx || !blk_cnt || !out || !lse || !dout || !delta || !sel_bits || !col_idx ||
+      !col_cnt || !dq || !dk || !dv)
+    return SA_ERR_NULL;
+  if (ap && (!tail || !dk_bar || !dv_bar)) return SA_ERR_NULL;
+  const void* al[] = {q, k, v, blk_idx, blk_cnt, out, lse, dout, delta, sel_bits, col_idx, col_cnt, dq, dk, dv};
+  for (const void* p : al)
+    if (!aligned16(p)) return SA_ERR_ALIGN;
+  if (ap && (!aligned16(tail) || !aligned16(dk_bar) || !aligned16(dv_bar))) return SA_ERR_ALIGN;
+  sa::BwdParams p;
+  p.scale = resolve_scale(desc);
+  p.causal = desc->causal;
+  p.approx = desc->approx;
+  sa::BwdPtrs x;
+  x.q = q;
+  x.k = k;
+  x.v = v;
+  x.tail = ap ? tail : nullptr;
+  x.out = out;
+  x.dout = dout;
+  x.blk_idx = blk_idx;
+  x.blk_cnt = blk_cnt;
+  x.lse = lse;
+  x.delta = delta;
+  x.sel_bits = sel_bits;
+  x.col_idx = col_idx;
+  x.col_cnt = col_cnt;
+  x.dk_bar = ap ? dk_bar : nullptr;
+  x.dv_bar = ap ? dv_bar : nullptr;
+  x.dq = dq;
+  x.dk = dk;
+  x.dv = dv;
+  return from_hip(sa::launch_bwd(s, p, x, (hipStream_t)stream));
+}
+
+SA_EXPORT sa_status sparse_attn_fwd_lse(const sa_desc* desc, const void* q, const void* k, const void* v,
+                                        const float* k_bar, const float* v_sum, const void* tail,
+                                        const int32_t* blk_idx, const int32_t* blk_cnt, void* out,
+                                        float* lse, void* stream) {
+  if (!lse) return SA_ERR_NULL;
+  return fwd_impl(desc, q, k, v, k_bar, v_sum, tail, blk_idx, blk_cnt, out, lse, stream);
 }

@@ -79,6 +79,7 @@ struct FwdArgs {
   const int32_t* idx;
   const int32_t* cnt;
   uint16_t* out;
+  float* lse;
   int Hq, Hkv, N, M, G, total;
   float scale_log2;  // scale * log2(e)
   int causal, approx;
@@ -583,6 +584,8 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
   // d = 32*nt + 8*(r/4) + 4*hh + (r%4).
   const float lt = half_sum(st.l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  // log of the denominator: sum_a exp(z_a) = lt * 2^m
+  if (a.lse && q_ok && hh == 0) a.lse[(size_t)bh * a.N + q_tok] = __logf(lt) + st.m * 0.69314718055994531f;
   if (q_ok) {
     uint16_t* orow = a.out + ((size_t)bh * a.N + q_tok) * D;
 #pragma unroll
@@ -625,6 +628,7 @@ hipError_t launch_fwd(const Shape& s, const FwdParams& p, const void* q, const v
   a.idx = blk_idx;
   a.cnt = blk_cnt;
   a.out = static_cast<uint16_t*>(out);
+  a.lse = p.lse;
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;
   a.N = s.N;

@@ -43,6 +43,7 @@ struct Args {
   const int32_t* idx;
   const int32_t* cnt;
   uint16_t* out;
+  float* lse;
   int Hq, Hkv, N, M, G, total;
   float scale_log2;
   int causal, approx;
@@ -422,6 +423,8 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
   // ---- epilogue: register r of d-tile nt holds d = 16*nt + 4*lg + r
   const float lt = row_sum4(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  // log of the denominator: sum_a exp(z_a) = lt * 2^m
+  if (a.lse && q_ok && lg == 0) a.lse[(size_t)bh * a.N + q_tok] = __logf(lt) + m * 0.69314718055994531f;
   if (q_ok) {
     uint16_t* orow = a.out + ((size_t)bh * a.N + q_tok) * D;
 #pragma unroll
@@ -456,6 +459,7 @@ hipError_t launch_fwd_w16(const Shape& s, const FwdParams& p, const void* q, con
   a.idx = blk_idx;
   a.cnt = blk_cnt;
   a.out = static_cast<uint16_t*>(out);
+  a.lse = p.lse;
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;
   a.N = s.N;

@@ -1,0 +1,725 @@
+// Gradients of stage 3 (bf16 inputs): dq, dk, dv of the block-sparse
+// attention with the 0th-order tail, for the selection the forward used.
+//
+// PISA explainer, "minimal documented usage": the 0th-order variant is the
+// one meant for training, so gradients flow through the exact blocks and
+// through the pooled pseudo-keys of the tail; the block selection is held
+// fixed (it passes no gradient).  With P_ia the softmax weight of key a
+// (token j of a listed block, or pooled block J with multiplicity n_J:
+// P = n_J exp(z - L)), u_a its value (v_j, or the bf16 block mean of v) and
+// dO the output gradient:
+//     dz_ia = P_ia (dO_i . u_a - D_i),   D_i = dO_i . o_i
+//     dq_i  = scale sum_a dz_ia key_a
+//     dk_j  = scale sum_i dz_ij q_i,  dv_j = sum_i P_ij dO_i      (exact)
+//     dkbar_J = scale sum_i dz_iJ q_i, dubar_J = sum_i P_iJ dO_i (pooled)
+// and the block means spread dkbar_J / n_J and dubar_J / n_J over the
+// tokens of block J.  The forward's log-denominator L_i (written by
+// sparse_attn_fwd_lse) gives P without a running max: exp2(z log2 e - L log2 e).
+//
+// Kernels (one launch each, in order):
+//   bwd_delta   D_i = dO_i . o_i (float32)
+//   bwd_bitmap  the selection as bits, one row per (batch, query head, block)
+//   bwd_cols    per (batch, KV group, key block J): the (query head, query
+//               block) pairs that list J, ascending (the transposed lists)
+//   bwd_dq      per query block, like the forward: its listed blocks, then
+//               its unlisted eligible pooled rows (gathered), tile by tile:
+//               S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T
+//   bwd_dtail   per KV group and 64 pooled rows: every query block whose tail
+//               holds them: S = Q Kbar^T, dP = dO Vbar^T, dVbar^T += dO^T P,
+//               dKbar^T += Q^T dS (float32 results)
+//   bwd_dkv     per key block: the pairs of its transposed list, tile by tile,
+//               dV^T += dO^T P, dK^T += Q^T dS; adds the pooled gradients
+//               of its block / n_J and writes dk, dv
+// All products are v_mfma_f32_16x16x32_bf16 with 16 rows (queries, keys or
+// pooled rows) per wave held in registers and 64-row tiles of the other
+// operand in LDS (HBM -> LDS by buffer loads into LDS).  One XOR swizzle of
+// the 16-byte chunks serves both LDS read patterns (row fragments with
+// ds_read_b128, transposed fragments with ds_read_b64_tr_b16).
+#include <math.h>
+
+#include "attn_common.h"
+#include "device_common.h"
+#include "launch.h"
+
+namespace sa {
+namespace {
+
+constexpr int BT = 64;   // rows per LDS tile (keys, queries or pooled rows)
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+struct BC {
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;         // bytes per row
+  static constexpr int RPK = 1024 / ROWB;    // rows per 1 KB DMA instruction
+  static constexpr int NKS = D / 32;         // 32-wide d steps
+  static constexpr int NOT = D / 16;         // 16-wide d tiles
+  static constexpr int TB = BT * ROWB;       // bytes of one tile
+};
+
+// Chunk c of row r sits at chunk swz(r, c): rows 0..15 of one chunk column
+// land on 16 different chunks (row fragments), and rows 0..7 (8..15) of two
+// adjacent chunk columns on 16 different chunks (transposed fragments).
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  return c ^ ((((r & 7) << 1) | ((r >> 3) & 1)) & (BC<D>::CPR - 1));
+}
+
+// ---- tile DMA: instruction i of wave w fills LDS bytes [(i*NW + w) KB, +1 KB)
+// = rows (i*NW + w)*RPK + lane/CPR; the row step per instruction is a
+// multiple of 16, so the swizzled column of a lane is the same for every i.
+template <int D, int NW>
+struct Dma {
+  static constexpr int NI = BT * BC<D>::CPR / (64 * NW);
+  static_assert(NI >= 1 && (NW * BC<D>::RPK) % 16 == 0, "tile DMA layout");
+  __device__ static int row0(int w, int lane) { return w * BC<D>::RPK + lane / BC<D>::CPR; }
+  __device__ static int col(int w, int lane) { return swz<D>(row0(w, lane), lane % BC<D>::CPR) * 16; }
+  // BT consecutive rows from byte `off` of the resource
+  __device__ static void tile(__amdgpu_buffer_rsrc_t rs, int off, char* lds, int w, int voff) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (i * NW + w) * 1024), 16, voff,
+                                               off + i * NW * 1024, 0, 0);
+  }
+  // rows at per-lane byte offsets ro[i]
+  __device__ static void rows(__amdgpu_buffer_rsrc_t rs, const int (&ro)[NI], int col, char* lds, int w) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (i * NW + w) * 1024), 16, ro[i] + col, 0, 0,
+                                               0);
+  }
+};
+
+// LDS offsets of this lane's fragments (tile-invariant): row fragments
+// (rows lr, chunk 4s + lg) and transposed fragments (rows 4*lg + lr/4 of a
+// 16-row half, columns 16*nt + 4*(lr & 3)).
+template <int D>
+struct Frag {
+  int rb[BC<D>::NKS];
+  int tb[BC<D>::NOT];
+  __device__ Frag(int lr, int lg) {
+#pragma unroll
+    for (int s = 0; s < BC<D>::NKS; ++s) rb[s] = lr * BC<D>::ROWB + swz<D>(lr, 4 * s + lg) * 16;
+    const int jr = 4 * lg + (lr >> 2);
+#pragma unroll
+    for (int nt = 0; nt < BC<D>::NOT; ++nt) {
+      const int n = 16 * nt + 4 * (lr & 3);
+      tb[nt] = jr * BC<D>::ROWB + swz<D>(jr, n >> 3) * 16 + (n & 7) * 2;
+    }
+  }
+};
+
+// acc[tg] = T_rows(16tg..16tg+15) . R^T: lane (lr, lg), register r = tile row
+// 16tg + 4lg + r against register row lr.
+template <int D>
+__device__ __forceinline__ void gemm_rows(f32x4 (&acc)[4], const char* tile, const Frag<D>& f,
+                                          const bf16x8 (&rg)[BC<D>::NKS]) {
+#pragma unroll
+  for (int tg = 0; tg < 4; ++tg) acc[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < BC<D>::NKS; ++s)
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(tile + f.rb[s] + 16 * tg * BC<D>::ROWB);
+      acc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rg[s], acc[tg], 0, 0, 0);
+    }
+}
+
+// acc[nt] += T^T(d-tile nt) . X, X packed from a gemm_rows-shaped array
+// (pk[cc]: tile rows of row groups 2cc and 2cc+1).
+template <int D>
+__device__ __forceinline__ void gemm_tr(f32x4 (&acc)[BC<D>::NOT], const char* tile, const Frag<D>& f,
+                                        const bf16x8 (&pk)[2]) {
+#pragma unroll
+  for (int nt = 0; nt < BC<D>::NOT; ++nt)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const char* p = tile + f.tb[nt] + 32 * cc * BC<D>::ROWB;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * BC<D>::ROWB));
+      const bf16x8 a = __builtin_bit_cast(
+          bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[cc], acc[nt], 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void pack_rows(const f32x4 (&x)[4], bf16x8 (&pk)[2]) {
+  uint32_t wd[8];
+#pragma unroll
+  for (int tg = 0; tg < 4; ++tg) {
+    wd[2 * tg] = pack2(x[tg][0], x[tg][1]);
+    wd[2 * tg + 1] = pack2(x[tg][2], x[tg][3]);
+  }
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+    pk[cc] = __builtin_bit_cast(bf16x8, u32x4{wd[4 * cc], wd[4 * cc + 1], wd[4 * cc + 2], wd[4 * cc + 3]});
+}
+
+// one bf16 row fragment per 32-wide d step: row `row` (zeros if !ok)
+template <int D>
+__device__ __forceinline__ void load_row(bf16x8 (&dst)[BC<D>::NKS], const uint16_t* rowp, bool ok, int lg) {
+#pragma unroll
+  for (int s = 0; s < BC<D>::NKS; ++s) {
+    const u32x4 x = ok ? *reinterpret_cast<const u32x4*>(rowp + 32 * s + 8 * lg) : u32x4{0u, 0u, 0u, 0u};
+    dst[s] = __builtin_bit_cast(bf16x8, x);
+  }
+}
+
+struct BwdArgs {
+  const uint16_t *q, *k, *v, *out, *dout;
+  const uint16_t *tail_k, *tail_v;   // bf16 block means of k and v
+  const int32_t *idx, *cnt;
+  const float* lse;
+  float* delta;
+  uint32_t* bits;      // [B, Hq, M, W]
+  int32_t *col_idx, *col_cnt;   // [B, Hkv, M, G*M], [B, Hkv, M]
+  float *dk_bar, *dv_bar;       // [B, Hkv, M, D]
+  uint16_t *dq, *dk, *dv;
+  int B, Hq, Hkv, N, M, G, W, block;
+  float scale, scale_log2;
+  int causal, approx;
+};
+
+// ---------------------------------------------------------------- D_i
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8;                  // lanes per row (16 bytes each)
+  const long row = ((long)blockIdx.x * 256 + threadIdx.x) / LPR;
+  const int c = threadIdx.x % LPR;
+  const long rows = (long)a.B * a.Hq * a.N;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 o = *reinterpret_cast<const u32x4*>(a.out + row * D + 8 * c);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(a.dout + row * D + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(bf16_bits_to_f32(o[e] & 0xFFFFu), bf16_bits_to_f32(g[e] & 0xFFFFu), acc);
+      acc = fmaf(bf16_bits_to_f32(o[e] >> 16), bf16_bits_to_f32(g[e] >> 16), acc);
+    }
+  }
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, LPR);
+  if (row < rows && c == 0) a.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------- bitmap
+__global__ __launch_bounds__(64) void bwd_bitmap_kernel(BwdArgs a) {
+  __shared__ uint32_t bits[kMaxBlocks / 32];
+  const long row = blockIdx.x;                 // (b * Hq + h) * M + I
+  for (int i = threadIdx.x; i < a.W; i += 64) bits[i] = 0u;
+  __syncthreads();
+  const int n = a.cnt[row];
+  const int32_t* list = a.idx + row * a.M;
+  for (int e = threadIdx.x; e < n; e += 64) {
+    const int J = list[e];
+    atomicOr(&bits[J >> 5], 1u << (J & 31));
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < a.W; i += 64) a.bits[row * a.W + i] = bits[i];
+}
+
+// ------------------------------------------------------- transposed lists
+// One wave per (b, g, 32 key blocks): pair x = h_local * M + I in ascending
+// order; its bitmap word holds the 32 key blocks' bits.
+__global__ __launch_bounds__(64) void bwd_cols_kernel(BwdArgs a) {
+  const int lane = threadIdx.x;
+  const int wi = blockIdx.x % a.W;
+  const int grp = blockIdx.x / a.W;           // b * Hkv + g
+  const int b = grp / a.Hkv, g = grp - (grp / a.Hkv) * a.Hkv;
+  const int GM = a.G * a.M;
+  int count[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) count[j] = 0;
+  for (int x0 = 0; x0 < GM; x0 += 64) {
+    const int x = x0 + lane;
+    uint32_t word = 0u;
+    if (x < GM) {
+      const int hl = x / a.M, I = x - hl * a.M;
+      word = a.bits[(((long)b * a.Hq + g * a.G + hl) * a.M + I) * a.W + wi];
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int J = 32 * wi + j;
+      if (J >= a.M) break;
+      const bool in = (word >> j) & 1u;
+      const uint64_t bal = __ballot(in);
+      if (in) a.col_idx[((long)grp * a.M + J) * GM + count[j] + lanes_below(bal)] = x;
+      count[j] += __popcll(bal);
+    }
+  }
+  if (lane < 32 && 32 * wi + lane < a.M) {
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) c = lane == j ? count[j] : c;
+    a.col_cnt[(long)grp * a.M + 32 * wi + lane] = c;
+  }
+}
+
+// ---------------------------------------------------------------- dq
+template <int D, int BLK>
+__global__ __launch_bounds__(4 * BLK, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int NW = BLK / 16;
+  constexpr int NT = 64 * NW;
+  constexpr int SUB = BLK / BT;                // 64-key tiles per block
+  using C = BC<D>;
+  using DM = Dma<D, NW>;
+  __shared__ __attribute__((aligned(1024))) char Kt[C::TB];
+  __shared__ __attribute__((aligned(1024))) char Vt[C::TB];
+  __shared__ uint32_t selbits[kMaxBlocks / 32];
+  __shared__ uint16_t tail_rows[kMaxBlocks];
+
+  const int total = a.B * a.Hq * a.M;
+  const int item = xcd_local_item(blockIdx.x, total);
+  if (item < 0) return;
+  const int hg = item % a.G;
+  int rest = item / a.G;
+  const int I = a.M - 1 - rest % a.M;
+  rest /= a.M;
+  const int g = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  const int h = g * a.G + hg;
+  const int bh = b * a.Hq + h;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int q_tok = I * BLK + 16 * w + lr;
+  const bool q_ok = q_tok < a.N;
+  const size_t qrow = (size_t)bh * a.N + (q_ok ? q_tok : 0);
+
+  bf16x8 qf[C::NKS], gf[C::NKS];
+  load_row<D>(qf, a.q + qrow * D, q_ok, lg);
+  load_row<D>(gf, a.dout + qrow * D, q_ok, lg);
+  const float Lc = q_ok ? a.lse[qrow] * kLog2e : INFINITY;   // P = 0 on padding rows
+  const float Dd = q_ok ? a.delta[qrow] : 0.f;
+
+  const int n_sel = scalar_view(a.cnt)[(size_t)bh * a.M + I];
+  const const_i32* list = scalar_view(a.idx + ((size_t)bh * a.M + I) * a.M);
+  const int Jend = a.causal ? I + 1 : a.M;
+  const int last_n = a.N - (a.M - 1) * BLK;
+  const int n_rest = a.approx ? Jend - n_sel : 0;
+  const int n_tt = (n_rest + BT - 1) / BT;
+  int edge = 0;   // the last listed block needs the edge mask (ragged end / diagonal)
+  if (n_sel > 0) {
+    const int J = list[n_sel - 1];
+    edge = ((J + 1) * BLK > a.N || (a.causal && J >= I)) ? 1 : 0;
+  }
+  const int n_exact = SUB * n_sel;
+  const int n_plain = n_exact - SUB * edge;
+  const int n_tiles = n_exact + n_tt;
+  const float log2_blk = __log2f((float)BLK);
+  const float last_fix = (__log2f((float)last_n) - log2_blk) / a.scale_log2;
+
+  if (a.approx) {
+    for (int i = t; i < kMaxBlocks / 32; i += NT) selbits[i] = 0u;
+    __syncthreads();
+    for (int e = t; e < n_sel; e += NT) {
+      const int J = list[e];
+      atomicOr(&selbits[J >> 5], 1u << (J & 31));
+    }
+    __syncthreads();
+    if (w == 0) {
+      int base = 0;
+      for (int J0 = 0; J0 < Jend; J0 += 64) {
+        const int J = J0 + lane;
+        const int Jc = J < Jend ? J : 0;
+        const bool rest_J = J < Jend && !((selbits[Jc >> 5] >> (Jc & 31)) & 1u);
+        const uint64_t bal = __ballot(rest_J);
+        if (rest_J) tail_rows[base + lanes_below(bal)] = (uint16_t)J;
+        base += __popcll(bal);
+      }
+    }
+    __syncthreads();
+  }
+
+  const int head_bytes = a.N * C::ROWB;
+  const size_t kv_off = (size_t)(b * a.Hkv + g) * a.N * D;
+  const size_t pp_off = (size_t)(b * a.Hkv + g) * a.M * D;
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(a.v + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t tkrs = head_rsrc(a.approx ? a.tail_k + pp_off : a.k, a.M * C::ROWB);
+  const __amdgpu_buffer_rsrc_t tvrs = head_rsrc(a.approx ? a.tail_v + pp_off : a.v, a.M * C::ROWB);
+  const int row0 = DM::row0(w, lane);
+  const int col = DM::col(w, lane);
+  const int voff = row0 * C::ROWB + col;
+  const Frag<D> fr(lr, lg);
+
+  // tile e: exact (key = first token) or tail (key = tail tile index)
+  auto tile_key = [&](int e) -> int {
+    return e < n_exact ? list[e / SUB] * BLK + (e % SUB) * BT : e - n_exact;
+  };
+  auto issue = [&](int e, int key, bool is_v) {
+    char* dst = is_v ? Vt : Kt;
+    if (e < n_exact) {
+      DM::tile(is_v ? vrs : krs, key * C::ROWB, dst, w, voff);
+    } else {
+      int ro[DM::NI];
+#pragma unroll
+      for (int i = 0; i < DM::NI; ++i) {
+        const int r = BT * key + row0 + i * NW * C::RPK;
+        ro[i] = (r < n_rest ? (int)tail_rows[r] : 0) * C::ROWB;
+      }
+      DM::rows(is_v ? tvrs : tkrs, ro, col, dst, w);
+    }
+  };
+
+  f32x4 dq[C::NOT];
+#pragma unroll
+  for (int i = 0; i < C::NOT; ++i) dq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float c = a.scale_log2;
+
+  int key = n_tiles > 0 ? tile_key(0) : 0;
+  if (n_tiles > 0) {
+    issue(0, key, false);
+    issue(0, key, true);
+  }
+  wait_vm();
+  __syncthreads();
+  for (int e = 0; e < n_tiles; ++e) {
+    f32x4 s[4], dp[4];
+    gemm_rows<D>(s, Kt, fr, qf);
+    gemm_rows<D>(dp, Vt, fr, gf);
+    __syncthreads();                           // V tile free
+    const int key1 = e + 1 < n_tiles ? tile_key(e + 1) : 0;
+    if (e + 1 < n_tiles) issue(e + 1, key1, true);
+
+    // masks: register r of row group tg holds key key + 16*tg + 4*lg + r
+    float lb = 0.f;
+    if (e >= n_exact) {
+      lb = log2_blk;
+      if (e == n_tiles - 1) {                  // padding rows, short last block
+        const int lim = n_rest - BT * key - 4 * lg;
+        const int fix_kr = (last_n != BLK && tail_rows[n_rest - 1] == a.M - 1) ? lim - 1 : -1;
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kr = 16 * tg + r;
+            s[tg][r] = kr < lim ? (kr == fix_kr ? s[tg][r] + last_fix : s[tg][r]) : -INFINITY;
+          }
+      }
+    } else if (e >= n_plain) {                 // ragged end / causal diagonal
+      int lim = a.N - key;
+      if (a.causal) lim = min(lim, q_tok - key + 1);
+      lim -= 4 * lg;
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[tg][r] = 16 * tg + r < lim ? s[tg][r] : -INFINITY;
+    }
+    // P = exp2(z log2 e + lb - L log2 e), dS = P (dP - D)
+    const float off = lb - Lc;
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[tg][r], c, off));
+        s[tg][r] = p * (dp[tg][r] - Dd);
+      }
+    bf16x8 pk[2];
+    pack_rows(s, pk);
+    gemm_tr<D>(dq, Kt, fr, pk);                // dQ^T += K^T dS^T
+    __syncthreads();                           // K tile free
+    if (e + 1 < n_tiles) issue(e + 1, key1, false);
+    wait_vm();
+    __syncthreads();
+    key = key1;
+  }
+
+  if (q_ok) {
+    uint16_t* orow = a.dq + qrow * D;
+#pragma unroll
+    for (int nt = 0; nt < C::NOT; ++nt) {
+      const u32x2 x = {pack2(dq[nt][0] * a.scale, dq[nt][1] * a.scale),
+                       pack2(dq[nt][2] * a.scale, dq[nt][3] * a.scale)};
+      *reinterpret_cast<u32x2*>(orow + 16 * nt + 4 * lg) = x;
+    }
+  }
+}
+
+// --------------------------------------------------- dk/dv and pooled grads
+// Shared body: NW waves, 16 register rows each (keys or pooled rows); loops
+// over 64-row query tiles handed out by `next`.  POOLED: register rows are
+// pooled rows with per-lane log2 weight `lw` (-inf: not in this query
+// block's tail); otherwise key tokens with the causal mask on the diagonal.
+template <int D, int NW, bool POOLED>
+struct KvAcc {
+  f32x4 dk[BC<D>::NOT];
+  f32x4 dv[BC<D>::NOT];
+};
+
+template <int D, int NW, bool POOLED>
+__device__ __forceinline__ void kv_tile(const BwdArgs& a, KvAcc<D, NW, POOLED>& acc, const char* Qt, const char* Ot,
+                                        const float* Lt, const float* Dt, const Frag<D>& fr,
+                                        const bf16x8 (&kf)[BC<D>::NKS], const bf16x8 (&vf)[BC<D>::NKS],
+                                        int lg, float lw, int diag_lim) {
+  f32x4 s[4], dp[4];
+  gemm_rows<D>(s, Qt, fr, kf);                 // S  = Q K^T   (rows: queries)
+  gemm_rows<D>(dp, Ot, fr, vf);                // dP = dO V^T
+  const float c = a.scale_log2;
+#pragma unroll
+  for (int tg = 0; tg < 4; ++tg) {
+    const f32x4 L = *reinterpret_cast<const f32x4*>(Lt + 16 * tg + 4 * lg);
+    const f32x4 Dv = *reinterpret_cast<const f32x4*>(Dt + 16 * tg + 4 * lg);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float p = __builtin_amdgcn_exp2f(fmaf(s[tg][r], c, lw - L[r]));
+      // causal diagonal: query row (16tg + 4lg + r) sees the key only at or after it
+      if (!POOLED) p = 16 * tg + 4 * lg + r >= diag_lim ? p : 0.f;
+      s[tg][r] = p;
+      dp[tg][r] = p * (dp[tg][r] - Dv[r]);
+    }
+  }
+  bf16x8 pk[2], dk_[2];
+  pack_rows(s, pk);
+  pack_rows(dp, dk_);
+  gemm_tr<D>(acc.dv, Ot, fr, pk);              // dV^T += dO^T P
+  gemm_tr<D>(acc.dk, Qt, fr, dk_);             // dK^T += Q^T dS
+}
+
+// Query tile (rows q0.. of head bh) into Qt/Ot, L and D of its rows into
+// Lt/Dt (+inf / 0 past the end of the sequence); ends with a barrier.
+template <int D, int NW>
+__device__ __forceinline__ void load_query_tile(const BwdArgs& a, int bh, int q0, char* Qt, char* Ot, float* Lt,
+                                                float* Dt, int w, int voff) {
+  using DM = Dma<D, NW>;
+  const int head_bytes = a.N * BC<D>::ROWB;
+  const __amdgpu_buffer_rsrc_t qrs = head_rsrc(a.q + (size_t)bh * a.N * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t ors = head_rsrc(a.dout + (size_t)bh * a.N * D, head_bytes);
+  DM::tile(qrs, q0 * BC<D>::ROWB, Qt, w, voff);
+  DM::tile(ors, q0 * BC<D>::ROWB, Ot, w, voff);
+  const int t = threadIdx.x;
+  if (t < BT) {
+    const int qi = q0 + t;
+    const bool ok = qi < a.N;
+    Lt[t] = ok ? a.lse[(size_t)bh * a.N + qi] * kLog2e : INFINITY;
+    Dt[t] = ok ? a.delta[(size_t)bh * a.N + qi] : 0.f;
+  }
+  wait_vm();
+  __syncthreads();
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__(4 * BLK, 2) void bwd_dkv_kernel(BwdArgs a) {
+  constexpr int NW = BLK / 16;
+  constexpr int SUB = BLK / BT;
+  using C = BC<D>;
+  using DM = Dma<D, NW>;
+  __shared__ __attribute__((aligned(1024))) char Qt[C::TB];
+  __shared__ __attribute__((aligned(1024))) char Ot[C::TB];
+  __shared__ __attribute__((aligned(16))) float Lt[BT];
+  __shared__ __attribute__((aligned(16))) float Dt[BT];
+
+  const int total = a.B * a.Hkv * a.M;
+  const int item = xcd_local_item(blockIdx.x, total);
+  if (item < 0) return;
+  const int grp = item / a.M;                  // b * Hkv + g
+  const int J = item - grp * a.M;
+  const int b = grp / a.Hkv;
+  const int g = grp - b * a.Hkv;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int k_tok = J * BLK + 16 * w + lr;
+  const bool k_ok = k_tok < a.N;
+  const size_t krow = (size_t)grp * a.N + (k_ok ? k_tok : 0);
+  bf16x8 kf[C::NKS], vf[C::NKS];
+  load_row<D>(kf, a.k + krow * D, k_ok, lg);
+  load_row<D>(vf, a.v + krow * D, k_ok, lg);
+
+  const int voff = DM::row0(w, lane) * C::ROWB + DM::col(w, lane);
+  const Frag<D> fr(lr, lg);
+  KvAcc<D, NW, false> acc;
+#pragma unroll
+  for (int i = 0; i < C::NOT; ++i) {
+    acc.dk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc.dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int GM = a.G * a.M;
+  const int n_col = scalar_view(a.col_cnt)[(size_t)grp * a.M + J];
+  const const_i32* cl = scalar_view(a.col_idx + ((size_t)grp * a.M + J) * GM);
+  for (int e = 0; e < n_col; ++e) {
+    const int x = cl[e];
+    const int hl = x / a.M, I = x - hl * a.M;
+    const int bh = b * a.Hq + g * a.G + hl;
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      const int q0 = I * BLK + BT * u;
+      if (q0 >= a.N) break;
+      load_query_tile<D, NW>(a, bh, q0, Qt, Ot, Lt, Dt, w, voff);
+      // causal diagonal: row r of the tile (token q0 + r) sees key k_tok iff
+      // r >= k_tok - q0
+      const int diag_lim = (a.causal && I == J) ? k_tok - q0 : -BT;
+      kv_tile<D, NW, false>(a, acc, Qt, Ot, Lt, Dt, fr, kf, vf, lg, 0.f, diag_lim);
+      __syncthreads();
+    }
+  }
+
+  if (k_ok) {
+    const float n = (float)min(BLK, a.N - J * BLK);
+    uint16_t* kr = a.dk + krow * D;
+    uint16_t* vr = a.dv + krow * D;
+    const float* kb = a.dk_bar + ((size_t)grp * a.M + J) * D;
+    const float* vb = a.dv_bar + ((size_t)grp * a.M + J) * D;
+#pragma unroll
+    for (int nt = 0; nt < C::NOT; ++nt) {
+      const int d0 = 16 * nt + 4 * lg;
+      f32x4 x = acc.dk[nt] * a.scale, y = acc.dv[nt];
+      if (a.approx) {   // the pooled key / mean value of this block, spread over its tokens
+        const f32x4 pk = *reinterpret_cast<const f32x4*>(kb + d0);
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(vb + d0);
+        x += pk / n;
+        y += pv / n;
+      }
+      *reinterpret_cast<u32x2*>(kr + d0) = u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])};
+      *reinterpret_cast<u32x2*>(vr + d0) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+    }
+  }
+}
+
+// Pooled gradients: workgroup per (b, g, 64 pooled rows), four waves.
+template <int D, int BLK>
+__global__ __launch_bounds__(256, 2) void bwd_dtail_kernel(BwdArgs a) {
+  constexpr int NW = 4;
+  constexpr int SUB = BLK / BT;
+  using C = BC<D>;
+  using DM = Dma<D, NW>;
+  __shared__ __attribute__((aligned(1024))) char Qt[C::TB];
+  __shared__ __attribute__((aligned(1024))) char Ot[C::TB];
+  __shared__ __attribute__((aligned(16))) float Lt[BT];
+  __shared__ __attribute__((aligned(16))) float Dt[BT];
+
+  const int tiles = (a.M + BT - 1) / BT;
+  const int grp = blockIdx.x / tiles;          // b * Hkv + g
+  const int pt = blockIdx.x - grp * tiles;
+  const int b = grp / a.Hkv;
+  const int g = grp - b * a.Hkv;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int Jl = BT * pt + 16 * w + lr;        // this lane's pooled row
+  const bool j_ok = Jl < a.M;
+  const size_t prow = (size_t)grp * a.M + (j_ok ? Jl : 0);
+  bf16x8 kf[C::NKS], vf[C::NKS];
+  load_row<D>(kf, a.tail_k + prow * D, j_ok, lg);
+  load_row<D>(vf, a.tail_v + prow * D, j_ok, lg);
+  const int nJ = Jl == a.M - 1 ? a.N - (a.M - 1) * a.block : a.block;
+  const float lw_in = __log2f((float)nJ);
+
+  const int voff = DM::row0(w, lane) * C::ROWB + DM::col(w, lane);
+  const Frag<D> fr(lr, lg);
+  KvAcc<D, NW, true> acc;
+#pragma unroll
+  for (int i = 0; i < C::NOT; ++i) {
+    acc.dk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc.dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // query blocks whose eligible range reaches these pooled rows
+  const int I0 = a.causal ? BT * pt : 0;
+  for (int hl = 0; hl < a.G; ++hl) {
+    const int bh = b * a.Hq + g * a.G + hl;
+    for (int I = I0; I < a.M; ++I) {
+      // pooled row Jl is in the tail of (bh, I): eligible and not listed
+      const uint32_t word = a.bits[((size_t)bh * a.M + I) * a.W + (j_ok ? Jl >> 5 : 0)];
+      const bool in = j_ok && (!a.causal || Jl <= I) && !((word >> (Jl & 31)) & 1u);
+      if (!__syncthreads_or(in)) continue;
+      const float lw = in ? lw_in : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        const int q0 = I * a.block + BT * u;
+        if (q0 >= a.N) break;
+        load_query_tile<D, NW>(a, bh, q0, Qt, Ot, Lt, Dt, w, voff);
+        kv_tile<D, NW, true>(a, acc, Qt, Ot, Lt, Dt, fr, kf, vf, lg, lw, 0);
+        __syncthreads();
+      }
+    }
+  }
+  if (j_ok) {
+    float* kb = a.dk_bar + prow * D;
+    float* vb = a.dv_bar + prow * D;
+#pragma unroll
+    for (int nt = 0; nt < C::NOT; ++nt) {
+      const int d0 = 16 * nt + 4 * lg;
+      *reinterpret_cast<f32x4*>(kb + d0) = acc.dk[nt] * a.scale;
+      *reinterpret_cast<f32x4*>(vb + d0) = acc.dv[nt];
+    }
+  }
+}
+
+template <int D, int BLK>
+hipError_t run_bwd(const BwdArgs& a, hipStream_t st) {
+  const long rows = (long)a.B * a.Hq * a.N;
+  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bwd_bitmap_kernel, dim3(a.B * a.Hq * a.M), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(bwd_cols_kernel, dim3(a.B * a.Hkv * a.W), dim3(64), 0, st, a);
+  const int nq = a.B * a.Hq * a.M;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BLK>), dim3(8 * ((nq + 7) / 8)), dim3(4 * BLK), 0, st, a);
+  if (a.approx) {
+    const int tiles = (a.M + BT - 1) / BT;
+    hipLaunchKernelGGL((bwd_dtail_kernel<D, BLK>), dim3(a.B * a.Hkv * tiles), dim3(256), 0, st, a);
+  }
+  const int nk = a.B * a.Hkv * a.M;
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, BLK>), dim3(8 * ((nk + 7) / 8)), dim3(4 * BLK), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+BwdSizes bwd_sizes(const Shape& s, int approx) {
+  BwdSizes z{};
+  const size_t W = (size_t)(s.M + 31) / 32;
+  z.lse = (size_t)s.B * s.Hq * s.N * sizeof(float);
+  z.delta = z.lse;
+  z.sel_bits = (size_t)s.B * s.Hq * s.M * W * sizeof(uint32_t);
+  z.col_idx = (size_t)s.B * s.Hq * s.M * s.M * sizeof(int32_t);
+  z.col_cnt = (size_t)s.B * s.Hkv * s.M * sizeof(int32_t);
+  z.dk_bar = approx ? (size_t)s.B * s.Hkv * s.M * s.D * sizeof(float) : 0;
+  z.dv_bar = z.dk_bar;
+  return z;
+}
+
+hipError_t launch_bwd(const Shape& s, const BwdParams& p, const BwdPtrs& x, hipStream_t st) {
+  BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(x.q);
+  a.k = static_cast<const uint16_t*>(x.k);
+  a.v = static_cast<const uint16_t*>(x.v);
+  a.out = static_cast<const uint16_t*>(x.out);
+  a.dout = static_cast<const uint16_t*>(x.dout);
+  if (p.approx) {
+    a.tail_k = static_cast<const uint16_t*>(x.tail);
+    a.tail_v = a.tail_k + (size_t)s.B * s.Hkv * s.M * s.D;
+  }
+  a.idx = x.blk_idx;
+  a.cnt = x.blk_cnt;
+  a.lse = x.lse;
+  a.delta = x.delta;
+  a.bits = x.sel_bits;
+  a.col_idx = x.col_idx;
+  a.col_cnt = x.col_cnt;
+  a.dk_bar = x.dk_bar;
+  a.dv_bar = x.dv_bar;
+  a.dq = static_cast<uint16_t*>(x.dq);
+  a.dk = static_cast<uint16_t*>(x.dk);
+  a.dv = static_cast<uint16_t*>(x.dv);
+  a.B = s.B;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.N = s.N;
+  a.M = s.M;
+  a.G = s.Hq / s.Hkv;
+  a.W = (s.M + 31) / 32;
+  a.block = s.block;
+  a.scale = p.scale;
+  a.scale_log2 = p.scale * kLog2e;
+  a.causal = p.causal;
+  a.approx = p.approx;
+  if (s.D == 128) return s.block == 128 ? run_bwd<128, 128>(a, st) : run_bwd<128, 64>(a, st);
+  return s.block == 128 ? run_bwd<64, 128>(a, st) : run_bwd<64, 64>(a, st);
+}
+
+}  // namespace sa

@@ -31,6 +31,7 @@ struct FwdArgs {
   const int32_t* idx;
   const int32_t* cnt;
   float* out;
+  float* lse;
   int Hq, Hkv, N, M, block, total;
   float scale;
   int causal, approx;
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(FwdArgs a) {
 
   if (active) {
     const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+    if (a.lse) a.lse[(size_t)bh * a.N + qi] = st.m + logf(st.l);
     float* o = a.out + ((size_t)bh * a.N + qi) * D;
 #pragma unroll
     for (int c = 0; c < D; ++c) o[c] = st.o[c] * inv;
@@ -203,6 +205,7 @@ hipError_t launch_fwd_f32(const Shape& s, const FwdParams& p, const void* q, con
   a.idx = blk_idx;
   a.cnt = blk_cnt;
   a.out = static_cast<float*>(out);
+  a.lse = p.lse;
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;
   a.N = s.N;

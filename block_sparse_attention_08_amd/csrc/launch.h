@@ -40,10 +40,33 @@ struct FwdParams {
   float scale;
   int causal;
   int approx;
+  float* lse;   // optional [B, Hq, N]: natural log of each row's softmax denominator
 };
 hipError_t launch_fwd(const Shape& s, const FwdParams& p, const void* q, const void* k,
                       const void* v, const float* k_bar, const float* v_sum, const void* tail,
                       const int32_t* blk_idx, const int32_t* blk_cnt, void* out, hipStream_t st);
+
+// Gradients of stage 3 (bf16 inputs).
+struct BwdSizes {
+  size_t lse, delta, sel_bits, col_idx, col_cnt, dk_bar, dv_bar;
+};
+struct BwdParams {
+  float scale;
+  int causal;
+  int approx;
+};
+struct BwdPtrs {
+  const void *q, *k, *v, *tail, *out, *dout;
+  const int32_t *blk_idx, *blk_cnt;
+  const float* lse;
+  float* delta;
+  uint32_t* sel_bits;
+  int32_t *col_idx, *col_cnt;
+  float *dk_bar, *dv_bar;
+  void *dq, *dk, *dv;
+};
+BwdSizes bwd_sizes(const Shape& s, int approx);
+hipError_t launch_bwd(const Shape& s, const BwdParams& p, const BwdPtrs& x, hipStream_t st);
 
 // Largest number of key blocks per row the selection kernel supports.
 constexpr int kMaxBlocks = 2048;

@@ -90,7 +90,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 3
+#define SPARSE_ATTN_ABI_VERSION 4
 
 typedef enum {
   SA_OK = 0,
@@ -169,6 +169,48 @@ sa_status sparse_attn_fwd(const sa_desc* desc, const void* q, const void* k, con
                           const float* k_bar, const float* v_sum, const void* tail,
                           const int32_t* blk_idx, const int32_t* blk_cnt, void* out,
                           void* stream);
+
+/* ---- Training: gradients of stage 3 (PISA explainer, "minimal documented
+ * usage": the simplified 0th-order variant is the one that supports
+ * training).  Gradients flow through the listed blocks and through the
+ * pooled pseudo-keys of the tail (their block means spread dkbar_J / n_J and
+ * dvbar_J / n_J over the block's tokens); the selection is held fixed.
+ * bfloat16 inputs only (SA_ERR_UNSUPPORTED for float32). */
+
+/* sparse_attn_fwd that also writes lse [batch, heads_q, seq_len] float32:
+ * the natural log of each query row's softmax denominator (exact keys and
+ * pooled pseudo-keys with their multiplicity), which sparse_attn_bwd needs. */
+sa_status sparse_attn_fwd_lse(const sa_desc* desc, const void* q, const void* k, const void* v,
+                              const float* k_bar, const float* v_sum, const void* tail,
+                              const int32_t* blk_idx, const int32_t* blk_cnt, void* out, float* lse,
+                              void* stream);
+
+typedef struct {        /* bytes of the backward's caller-allocated buffers */
+  size_t lse;           /* [B, Hq, N] float32 (written by sparse_attn_fwd_lse)          */
+  size_t delta;         /* [B, Hq, N] float32 scratch: dO . o per row                   */
+  size_t sel_bits;      /* [B, Hq, M, ceil(M/32)] uint32 scratch: the selection as bits */
+  size_t col_idx;       /* [B, Hkv, M, (Hq/Hkv)*M] int32 scratch: transposed lists      */
+  size_t col_cnt;       /* [B, Hkv, M] int32 scratch                                     */
+  size_t dk_bar;        /* [B, Hkv, M, d] float32 scratch (0 unless approx)             */
+  size_t dv_bar;        /* [B, Hkv, M, d] float32 scratch (0 unless approx)             */
+} sa_bwd_sizes;
+
+/* Bytes of the backward buffers for `desc` (host only). */
+sa_status sparse_attn_bwd_buffer_sizes(const sa_desc* desc, sa_bwd_sizes* sizes);
+
+/* Gradients of sum(dout * out) with respect to q, k, v, for the lists the
+ * forward used (blk_idx / blk_cnt) and its out and lse.  Writes dq [B, Hq,
+ * N, d], dk and dv [B, Hkv, N, d] in bfloat16 (query heads of one KV group
+ * add into its dk, dv); uses delta, sel_bits, col_idx, col_cnt and, with
+ * approx, dk_bar / dv_bar as scratch (no initial contents needed).  `tail`
+ * is the pool pass's bf16 tail operands (approx only).  Lists must be
+ * strictly ascending and eligible, as for sparse_attn_fwd.  Errors as for
+ * the forward; SA_ERR_UNSUPPORTED for float32 inputs. */
+sa_status sparse_attn_bwd(const sa_desc* desc, const void* q, const void* k, const void* v,
+                          const void* tail, const int32_t* blk_idx, const int32_t* blk_cnt,
+                          const void* out, const float* lse, const void* dout, float* delta,
+                          uint32_t* sel_bits, int32_t* col_idx, int32_t* col_cnt, float* dk_bar,
+                          float* dv_bar, void* dq, void* dk, void* dv, void* stream);
 
 /* Static, human-readable text of a status code. */
 const char* sparse_attn_status_string(sa_status status);

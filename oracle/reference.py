@@ -210,12 +210,13 @@ def mask_to_lists(sel: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 def attend_block(q_rows: np.ndarray, row0: int, k: np.ndarray, v: np.ndarray,
                  k_bar: Optional[np.ndarray], v_sum: Optional[np.ndarray],
                  sel_row: np.ndarray, elig_row: np.ndarray, *, block: int, scale: float,
-                 causal: bool, approx: bool) -> np.ndarray:
+                 causal: bool, approx: bool, with_lse: bool = False):
     """Output rows for one (batch, head, query block).
 
     q_rows [nI, d] are the block's query tokens (token index row0 + r);
     k, v [N, d] the KV head; k_bar, v_sum [M, d] its pooled key / value sum.
-    Returns [nI, d] float64.
+    Returns [nI, d] float64 (and, with ``with_lse``, the natural log of each
+    row's denominator, [nI]).
     """
     N = k.shape[0]
     nI = q_rows.shape[0]
@@ -248,6 +249,9 @@ def attend_block(q_rows: np.ndarray, row0: int, k: np.ndarray, v: np.ndarray,
     out = np.zeros_like(num)
     ok = den > 0
     out[ok] = num[ok] / den[ok, None]
+    if with_lse:
+        with np.errstate(divide="ignore"):
+            return out, m + np.log(den)
     return out
 
 
@@ -267,7 +271,8 @@ def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, block: int, causal: 
     ``sel``: optional selection mask [B,Hq,M,M] to use instead of the
     oracle's own (e.g. density 1 / dense lists).
 
-    Returns a dict with q_bar, k_bar, v_sum, n, scores, mask, thresholds, out.
+    Returns a dict with q_bar, k_bar, v_sum, n, scores, mask, thresholds, out
+    and lse (natural log of each query row's softmax denominator).
     """
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -285,18 +290,20 @@ def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, block: int, causal: 
     t = thresholds(s, causal=causal, mode=mode, alpha=alpha, density=density)
     elig = eligible_mask(M, causal)
     out = np.full((B, Hq, N, d), np.nan)
+    lse = np.full((B, Hq, N), np.nan)
     todo = rows if rows is not None else [(b, h, I) for b in range(B) for h in range(Hq)
                                           for I in range(M)]
     bounds = block_bounds(N, block)
     for (b, h, I) in todo:
         g = kv_group(h, Hq, Hkv)
         r0, r1 = bounds[I]
-        out[b, h, r0:r1] = attend_block(
+        out[b, h, r0:r1], lse[b, h, r0:r1] = attend_block(
             q[b, h, r0:r1], r0, k[b, g], v[b, g],
             k_bar[b, g], None if v_sum is None else v_sum[b, g],
-            mask[b, h, I], elig[I], block=block, scale=scale, causal=causal, approx=approx)
+            mask[b, h, I], elig[I], block=block, scale=scale, causal=causal, approx=approx,
+            with_lse=True)
     return dict(q_bar=q_bar, k_bar=k_bar, v_sum=v_sum, n=block_sizes(N, block), scores=s,
-                mask=mask, thresholds=t, out=out)
+                mask=mask, thresholds=t, out=out, lse=lse)
 
 
 # --------------------------------------------------------------------------

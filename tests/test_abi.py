@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
     h = _lib.lib()
     for name in _declared():
         assert hasattr(h, name), name
-    assert bsa.abi_version() == 3
+    assert bsa.abi_version() == 4
 
 
 @pytest.mark.skipif(not os.path.exists(_lib.PEAKS_PATH), reason="libsa_peaks.so not built")

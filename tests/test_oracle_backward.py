@@ -98,3 +98,32 @@ def test_tail_only_gradient_spreads_evenly_over_block_tokens():
         assert np.allclose(g["dk"][0, 0, rows], g["dk"][0, 0, J * block])
         assert np.allclose(g["dv"][0, 0, rows], g["dv"][0, 0, J * block])
     assert not np.allclose(g["dk"][0, 0, 0], g["dk"][0, 0, 1])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_at_density_one_is_dense_logsumexp(causal):
+    """The forward's log-denominator at density 1 is torch's logsumexp of the
+    dense scaled scores (causally masked)."""
+    B, Hq, Hkv, N, d, block = 1, 2, 1, 70, 8, 16
+    q, k, v = random_qkv(B, Hq, Hkv, N, d, seed=24, block=block)
+    r = oracle.forward(q, k, v, block=block, causal=causal, approx=True, mode="density", density=1.0)
+    qt = torch.from_numpy(np.asarray(q, np.float64))
+    kt = torch.from_numpy(np.asarray(k, np.float64)).repeat_interleave(2, 1)
+    z = qt @ kt.transpose(-1, -2) / np.sqrt(d)
+    if causal:
+        z = z.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+    np.testing.assert_allclose(r["lse"], torch.logsumexp(z, -1).numpy(), atol=1e-12, rtol=0)
+
+
+def test_lse_with_tail_counts_block_multiplicity():
+    """Identical keys inside every block: the tail is exact, so the
+    log-denominator equals the dense one for any selection."""
+    B, Hq, Hkv, N, d, block = 1, 1, 1, 48, 4, 16
+    q, k, v = random_qkv(B, Hq, Hkv, N, d, seed=25, block=block)
+    k = np.repeat(np.asarray(k, np.float64)[:, :, ::block], block, axis=2)[:, :, :N]
+    sel = np.zeros((1, 1, 3, 3), bool)
+    sel[..., 1] = True
+    r = oracle.forward(q, k, v, block=block, causal=False, approx=True, mode="density", sel=sel)
+    z = np.asarray(q, np.float64)[0, 0] @ k[0, 0].T / np.sqrt(d)
+    ref = np.log(np.exp(z).sum(-1))
+    np.testing.assert_allclose(r["lse"][0, 0], ref, atol=1e-12, rtol=0)
