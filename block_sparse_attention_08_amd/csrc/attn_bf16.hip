@@ -154,8 +154,9 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int tile_off
 #pragma unroll
   for (int i = 0; i < C::NI; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (i * C::NW + w) * 1024), 16,
-                                             row0 * C::ROWB + col[i % DmaCfg<D, BLK>::NVAR],
-                                             tile_off + i * C::NW * 1024, 0, 0);
+                                             tile_off + i * C::NW * 1024 + row0 * C::ROWB +
+                                                 col[i % DmaCfg<D, BLK>::NVAR],
+                                             0, 0, 0);
 }
 
 // Gathered tile: instruction i copies this lane's chunk of the row at byte

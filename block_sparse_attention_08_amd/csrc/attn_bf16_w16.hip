@@ -85,8 +85,8 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, int tile_off
   using C = Cfg<D, BLK>;
 #pragma unroll
   for (int i = 0; i < C::NI; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (i * C::NW + w) * 1024), 16, lane_off,
-                                             tile_off + i * C::NW * 1024, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (i * C::NW + w) * 1024), 16,
+                                             tile_off + i * C::NW * 1024 + lane_off, 0, 0, 0);
 }
 
 // Gather: like dma_tile, but instruction i reads this lane's chunk of the

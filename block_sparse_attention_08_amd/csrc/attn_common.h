@@ -45,6 +45,9 @@ __device__ __forceinline__ const const_i32* scalar_view(const int32_t* p) {
 
 // Buffer resource over one [rows, D] bf16 head of `bytes` bytes: loads past
 // the end return zero (rows of a ragged last block, pooled rows past M).
+// The hardware range check of a raw buffer covers the per-lane offset plus
+// the instruction's immediate, not the scalar offset, so every load here
+// carries its whole offset in the per-lane operand and passes 0 as soffset.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
 }
