@@ -54,6 +54,8 @@ def parse():
                    help="also run one device copy of this size (counter calibration runs)")
     p.add_argument("--dense", action="store_true",
                    help="attend every eligible block (caller lists), the dense comparison run")
+    p.add_argument("--backward", action="store_true",
+                   help="also run the gradients (fwd_lse + bwd) each step and report them")
     p.add_argument("--fused-route", action="store_true",
                    help="pool + select in one cooperative launch (sparse_attn_route)")
     return p.parse_args()
@@ -203,6 +205,14 @@ def main():
                          causal=wl.causal, approx=wl.approx)
     ws = bsa.Workspace(desc, device=dev)
     out = torch.empty_like(qd)
+    if args.backward:
+        if wl.dtype != "bf16":
+            print("--backward needs a bf16 workload", file=sys.stderr)
+            sys.exit(2)
+        bws = bsa.BwdWorkspace(desc, device=dev)
+        gen = torch.Generator(device=dev).manual_seed(args.seed + 1)
+        dout = torch.randn(qd.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     M = wl.M
     dense_idx = dense_cnt = None
     if args.dense:
@@ -230,10 +240,16 @@ def main():
                 ev[2].record()
         if args.dense:
             bsa.fwd(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, dense_idx, dense_cnt, out)
+        elif args.backward:
+            bsa.fwd_lse(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, ws.blk_idx, ws.blk_cnt, out, bws.lse)
         else:
             bsa.fwd(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, ws.blk_idx, ws.blk_cnt, out)
         if ev:
             ev[3].record()
+        if args.backward:
+            bsa.bwd(desc, qd, kd, vd, ws.tail, ws.blk_idx, ws.blk_cnt, out, dout, bws, dq, dk, dv)
+            if ev:
+                ev[4].record()
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -248,7 +264,7 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {wl.name}: warmup {args.warmup} done", file=sys.stderr, flush=True)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -323,6 +339,14 @@ def main():
                                         * (0.5 if wl.causal else 1.0) / (ms_step * 1e-3) / 1e12, 2),
         },
     }
+    if args.backward:
+        ms_bwd = np.mean([e[3].elapsed_time(e[4]) for e in evs])
+        bflops = 10.0 * wl.d * (ex + tl)      # S, dP, dV, dK, dQ: 2d each per pair
+        result["backward"] = {
+            "bwd_ms": round(ms_bwd, 4), "algorithmic_gflop": round(bflops / 1e9, 3),
+            "TFLOPs": round(bflops / (ms_bwd * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(bflops / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "note": "step = pool + select + fwd_lse + bwd; value/ms_per_step include the backward"}
     if not args.no_peaks:
         print("[bench] measuring achievable HBM read and bf16 MFMA rates", file=sys.stderr, flush=True)
         hbm, mfma = achievable_peaks(dev)

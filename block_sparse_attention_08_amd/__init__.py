@@ -155,12 +155,12 @@ class BwdWorkspace:
         f32, i32 = torch.float32, torch.int32
         W = -(-M // 32)
         self.lse = torch.empty((B, Hq, N), dtype=f32, device=device)
-        self.delta = torch.empty((B, Hq, N), dtype=f32, device=device)
+        self.delta = torch.empty(sz["delta"] // 4, dtype=f32, device=device)
         self.sel_bits = torch.empty((B, Hq, M, W), dtype=i32, device=device)
         self.col_idx = torch.empty(sz["col_idx"] // 4, dtype=i32, device=device)
         self.col_cnt = torch.empty((B, Hkv, M), dtype=i32, device=device)
-        self.dk_bar = torch.empty((B, Hkv, M, d), dtype=f32, device=device) if sz["dk_bar"] else None
-        self.dv_bar = torch.empty((B, Hkv, M, d), dtype=f32, device=device) if sz["dv_bar"] else None
+        self.dk_bar = torch.empty(sz["dk_bar"] // 4, dtype=f32, device=device) if sz["dk_bar"] else None
+        self.dv_bar = torch.empty(sz["dv_bar"] // 4, dtype=f32, device=device) if sz["dv_bar"] else None
         assert self.sel_bits.numel() * 4 == sz["sel_bits"] and self.lse.numel() * 4 == sz["lse"]
 
 

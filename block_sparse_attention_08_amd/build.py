@@ -44,6 +44,7 @@ CXXFLAGS = [
 FILE_FLAGS = {
     "attn_bf16.hip": ["-fno-honor-nans"],
     "attn_bf16_w16.hip": ["-fno-honor-nans"],
+    "attn_bwd.hip": ["-fno-honor-nans"],
 }
 
 

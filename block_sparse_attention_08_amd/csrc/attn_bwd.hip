@@ -17,19 +17,20 @@
 // sparse_attn_fwd_lse) gives P without a running max: exp2(z log2 e - L log2 e).
 //
 // Kernels (one launch each, in order):
-//   bwd_delta   D_i = dO_i . o_i (float32)
+//   bwd_delta   D_i = dO_i . o_i and L_i log2 e (float32)
 //   bwd_bitmap  the selection as bits, one row per (batch, query head, block)
 //   bwd_cols    per (batch, KV group, key block J): the (query head, query
 //               block) pairs that list J, ascending (the transposed lists)
 //   bwd_dq      per query block, like the forward: its listed blocks, then
 //               its unlisted eligible pooled rows (gathered), tile by tile:
 //               S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T
-//   bwd_dtail   per KV group and 64 pooled rows: every query block whose tail
-//               holds them: S = Q Kbar^T, dP = dO Vbar^T, dVbar^T += dO^T P,
-//               dKbar^T += Q^T dS (float32 results)
+//   bwd_dtail   per KV group, 64 pooled rows and one of 16 ranges of query
+//               blocks: every query block of the range whose tail holds
+//               them: S = Q Kbar^T, dP = dO Vbar^T, dVbar^T += dO^T P,
+//               dKbar^T += Q^T dS (float32 partial sums per range)
 //   bwd_dkv     per key block: the pairs of its transposed list, tile by tile,
 //               dV^T += dO^T P, dK^T += Q^T dS; adds the pooled gradients
-//               of its block / n_J and writes dk, dv
+//               of its block (the 16 partial sums) / n_J and writes dk, dv
 // All products are v_mfma_f32_16x16x32_bf16 with 16 rows (queries, keys or
 // pooled rows) per wave held in registers and 64-row tiles of the other
 // operand in LDS (HBM -> LDS by buffer loads into LDS).  One XOR swizzle of
@@ -45,6 +46,7 @@ namespace sa {
 namespace {
 
 constexpr int BT = 64;   // rows per LDS tile (keys, queries or pooled rows)
+constexpr int kTailChunks = 16;   // query-block ranges of the pooled-gradient pass
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
@@ -78,8 +80,8 @@ struct Dma {
   __device__ static void tile(__amdgpu_buffer_rsrc_t rs, int off, char* lds, int w, int voff) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (i * NW + w) * 1024), 16, voff,
-                                               off + i * NW * 1024, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (i * NW + w) * 1024), 16,
+                                               off + i * NW * 1024 + voff, 0, 0, 0);
   }
   // rows at per-lane byte offsets ro[i]
   __device__ static void rows(__amdgpu_buffer_rsrc_t rs, const int (&ro)[NI], int col, char* lds, int w) {
@@ -199,7 +201,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, LPR);
-  if (row < rows && c == 0) a.delta[row] = acc;
+  if (row < rows && c == 0) {
+    a.delta[row] = acc;
+    a.delta[rows + row] = a.lse[row] * kLog2e;   // log-denominator in log2 units
+  }
 }
 
 // ---------------------------------------------------------------- bitmap
@@ -291,7 +296,7 @@ __global__ __launch_bounds__(4 * BLK, 2) void bwd_dq_kernel(BwdArgs a) {
   bf16x8 qf[C::NKS], gf[C::NKS];
   load_row<D>(qf, a.q + qrow * D, q_ok, lg);
   load_row<D>(gf, a.dout + qrow * D, q_ok, lg);
-  const float Lc = q_ok ? a.lse[qrow] * kLog2e : INFINITY;   // P = 0 on padding rows
+  const float Lc = q_ok ? a.delta[(size_t)a.B * a.Hq * a.N + qrow] : INFINITY;   // P = 0 on padding rows
   const float Dd = q_ok ? a.delta[qrow] : 0.f;
 
   const int n_sel = scalar_view(a.cnt)[(size_t)bh * a.M + I];
@@ -478,26 +483,24 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, KvAcc<D, NW, POOLED>& 
   gemm_tr<D>(acc.dk, Qt, fr, dk_);             // dK^T += Q^T dS
 }
 
-// Query tile (rows q0.. of head bh) into Qt/Ot, L and D of its rows into
-// Lt/Dt (+inf / 0 past the end of the sequence); ends with a barrier.
+// Query tile (rows q0.. of head bh) into Qt/Ot, the L log2 e and D values
+// of its rows into Lt/Dt, all by loads into LDS (waves 0 and 1 move the 64
+// floats).  Rows past the end of the sequence read zeros: Q and dO rows of
+// zero make P dO, dP and D zero there, so such rows add nothing.
 template <int D, int NW>
-__device__ __forceinline__ void load_query_tile(const BwdArgs& a, int bh, int q0, char* Qt, char* Ot, float* Lt,
-                                                float* Dt, int w, int voff) {
+__device__ __forceinline__ void issue_query_tile(const BwdArgs& a, int bh, int q0, char* Qt, char* Ot, float* Lt,
+                                                 float* Dt, int w, int voff) {
   using DM = Dma<D, NW>;
   const int head_bytes = a.N * BC<D>::ROWB;
-  const __amdgpu_buffer_rsrc_t qrs = head_rsrc(a.q + (size_t)bh * a.N * D, head_bytes);
-  const __amdgpu_buffer_rsrc_t ors = head_rsrc(a.dout + (size_t)bh * a.N * D, head_bytes);
-  DM::tile(qrs, q0 * BC<D>::ROWB, Qt, w, voff);
-  DM::tile(ors, q0 * BC<D>::ROWB, Ot, w, voff);
-  const int t = threadIdx.x;
-  if (t < BT) {
-    const int qi = q0 + t;
-    const bool ok = qi < a.N;
-    Lt[t] = ok ? a.lse[(size_t)bh * a.N + qi] * kLog2e : INFINITY;
-    Dt[t] = ok ? a.delta[(size_t)bh * a.N + qi] : 0.f;
+  DM::tile(head_rsrc(a.q + (size_t)bh * a.N * D, head_bytes), q0 * BC<D>::ROWB, Qt, w, voff);
+  DM::tile(head_rsrc(a.dout + (size_t)bh * a.N * D, head_bytes), q0 * BC<D>::ROWB, Ot, w, voff);
+  if (w < 2) {
+    const long rows = (long)a.B * a.Hq * a.N;
+    const float* src = (w == 0 ? a.delta + rows : a.delta) + (size_t)bh * a.N;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, a.N * 4, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(w == 0 ? Lt : Dt), 4, q0 * 4 + (threadIdx.x & 63) * 4, 0, 0,
+                                             0);
   }
-  wait_vm();
-  __syncthreads();
 }
 
 template <int D, int BLK>
@@ -506,10 +509,16 @@ __global__ __launch_bounds__(4 * BLK, 2) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int SUB = BLK / BT;
   using C = BC<D>;
   using DM = Dma<D, NW>;
-  __shared__ __attribute__((aligned(1024))) char Qt[C::TB];
-  __shared__ __attribute__((aligned(1024))) char Ot[C::TB];
-  __shared__ __attribute__((aligned(16))) float Lt[BT];
-  __shared__ __attribute__((aligned(16))) float Dt[BT];
+  // double-buffered query tiles (Q, dO, and the L, D of their rows), each
+  // buffer a separate LDS object named statically in the unrolled loop
+  __shared__ __attribute__((aligned(1024))) char Q0[C::TB];
+  __shared__ __attribute__((aligned(1024))) char Q1[C::TB];
+  __shared__ __attribute__((aligned(1024))) char O0[C::TB];
+  __shared__ __attribute__((aligned(1024))) char O1[C::TB];
+  __shared__ __attribute__((aligned(16))) float L0[BT];
+  __shared__ __attribute__((aligned(16))) float L1[BT];
+  __shared__ __attribute__((aligned(16))) float D0[BT];
+  __shared__ __attribute__((aligned(16))) float D1[BT];
 
   const int total = a.B * a.Hkv * a.M;
   const int item = xcd_local_item(blockIdx.x, total);
@@ -542,27 +551,53 @@ __global__ __launch_bounds__(4 * BLK, 2) void bwd_dkv_kernel(BwdArgs a) {
   const int GM = a.G * a.M;
   const int n_col = scalar_view(a.col_cnt)[(size_t)grp * a.M + J];
   const const_i32* cl = scalar_view(a.col_idx + ((size_t)grp * a.M + J) * GM);
-  for (int e = 0; e < n_col; ++e) {
-    const int x = cl[e];
-    const int hl = x / a.M, I = x - hl * a.M;
-    const int bh = b * a.Hq + g * a.G + hl;
-#pragma unroll
-    for (int u = 0; u < SUB; ++u) {
-      const int q0 = I * BLK + BT * u;
-      if (q0 >= a.N) break;
-      load_query_tile<D, NW>(a, bh, q0, Qt, Ot, Lt, Dt, w, voff);
-      // causal diagonal: row r of the tile (token q0 + r) sees key k_tok iff
-      // r >= k_tok - q0
-      const int diag_lim = (a.causal && I == J) ? k_tok - q0 : -BT;
-      kv_tile<D, NW, false>(a, acc, Qt, Ot, Lt, Dt, fr, kf, vf, lg, 0.f, diag_lim);
-      __syncthreads();
+  // tile t: sub-tile t % SUB of the query block of list entry t / SUB (a
+  // sub-tile past the end of the sequence has no valid rows: L = +inf there,
+  // so it adds nothing)
+  const int n_t = n_col * SUB;
+  auto tile_of = [&](int tt, int& bh, int& q0, int& I) {
+    const int x = cl[tt / SUB];
+    const int hl = x / a.M;
+    I = x - hl * a.M;
+    bh = b * a.Hq + g * a.G + hl;
+    q0 = I * BLK + BT * (tt % SUB);
+  };
+
+  int bh0 = 0, q00 = 0, I0 = 0;
+  if (n_t > 0) {
+    tile_of(0, bh0, q00, I0);
+    issue_query_tile<D, NW>(a, bh0, q00, Q0, O0, L0, D0, w, voff);
+  }
+  wait_vm();
+  __syncthreads();
+  // one tile: Qc/Oc/Lc/Dc hold tile tt; tile tt+1 goes to Qn/On/Ln/Dn
+  auto step = [&](int tt, const char* Qc, const char* Oc, const float* Lc, const float* Dc, char* Qn, char* On,
+                  float* Ln, float* Dn) __attribute__((always_inline)) {
+    int bh1 = 0, q01 = 0, I1 = 0;
+    if (tt + 1 < n_t) {
+      tile_of(tt + 1, bh1, q01, I1);
+      issue_query_tile<D, NW>(a, bh1, q01, Qn, On, Ln, Dn, w, voff);
     }
+    // causal diagonal: row r of the tile (token q0 + r) sees key k_tok iff
+    // r >= k_tok - q0
+    const int diag_lim = (a.causal && I0 == J) ? k_tok - q00 : -BT;
+    kv_tile<D, NW, false>(a, acc, Qc, Oc, Lc, Dc, fr, kf, vf, lg, 0.f, diag_lim);
+    wait_vm();
+    __syncthreads();
+    bh0 = bh1;
+    q00 = q01;
+    I0 = I1;
+  };
+  for (int tt = 0; tt < n_t; tt += 2) {
+    step(tt, Q0, O0, L0, D0, Q1, O1, L1, D1);
+    if (tt + 1 < n_t) step(tt + 1, Q1, O1, L1, D1, Q0, O0, L0, D0);
   }
 
   if (k_ok) {
     const float n = (float)min(BLK, a.N - J * BLK);
     uint16_t* kr = a.dk + krow * D;
     uint16_t* vr = a.dv + krow * D;
+    const size_t pstride = (size_t)a.B * a.Hkv * a.M * D;   // between chunks' partial sums
     const float* kb = a.dk_bar + ((size_t)grp * a.M + J) * D;
     const float* vb = a.dv_bar + ((size_t)grp * a.M + J) * D;
 #pragma unroll
@@ -570,8 +605,11 @@ __global__ __launch_bounds__(4 * BLK, 2) void bwd_dkv_kernel(BwdArgs a) {
       const int d0 = 16 * nt + 4 * lg;
       f32x4 x = acc.dk[nt] * a.scale, y = acc.dv[nt];
       if (a.approx) {   // the pooled key / mean value of this block, spread over its tokens
-        const f32x4 pk = *reinterpret_cast<const f32x4*>(kb + d0);
-        const f32x4 pv = *reinterpret_cast<const f32x4*>(vb + d0);
+        f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pv = {0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < kTailChunks; ++c) {
+          pk += *reinterpret_cast<const f32x4*>(kb + c * pstride + d0);
+          pv += *reinterpret_cast<const f32x4*>(vb + c * pstride + d0);
+        }
         x += pk / n;
         y += pv / n;
       }
@@ -594,8 +632,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dtail_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float Dt[BT];
 
   const int tiles = (a.M + BT - 1) / BT;
-  const int grp = blockIdx.x / tiles;          // b * Hkv + g
-  const int pt = blockIdx.x - grp * tiles;
+  const int chunk = blockIdx.x % kTailChunks;
+  const int grp = blockIdx.x / kTailChunks / tiles;   // b * Hkv + g
+  const int pt = blockIdx.x / kTailChunks - grp * tiles;
   const int b = grp / a.Hkv;
   const int g = grp - b * a.Hkv;
   const int t = threadIdx.x;
@@ -619,11 +658,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dtail_kernel(BwdArgs a) {
     acc.dk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     acc.dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // query blocks whose eligible range reaches these pooled rows
-  const int I0 = a.causal ? BT * pt : 0;
-  for (int hl = 0; hl < a.G; ++hl) {
+  // this workgroup's share of the (query head, query block) pairs x =
+  // hl * M + I; causal: only query blocks at or after these pooled rows
+  const int GM = a.G * a.M;
+  const int per = (GM + kTailChunks - 1) / kTailChunks;
+  const int x1 = min(GM, (chunk + 1) * per);
+  for (int x = chunk * per; x < x1; ++x) {
+    const int hl = x / a.M, I = x - hl * a.M;
+    if (a.causal && I < BT * pt) continue;
     const int bh = b * a.Hq + g * a.G + hl;
-    for (int I = I0; I < a.M; ++I) {
+    {
       // pooled row Jl is in the tail of (bh, I): eligible and not listed
       const uint32_t word = a.bits[((size_t)bh * a.M + I) * a.W + (j_ok ? Jl >> 5 : 0)];
       const bool in = j_ok && (!a.causal || Jl <= I) && !((word >> (Jl & 31)) & 1u);
@@ -633,15 +677,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dtail_kernel(BwdArgs a) {
       for (int u = 0; u < SUB; ++u) {
         const int q0 = I * a.block + BT * u;
         if (q0 >= a.N) break;
-        load_query_tile<D, NW>(a, bh, q0, Qt, Ot, Lt, Dt, w, voff);
+        issue_query_tile<D, NW>(a, bh, q0, Qt, Ot, Lt, Dt, w, voff);
+        wait_vm();
+        __syncthreads();
         kv_tile<D, NW, true>(a, acc, Qt, Ot, Lt, Dt, fr, kf, vf, lg, lw, 0);
         __syncthreads();
       }
     }
   }
-  if (j_ok) {
-    float* kb = a.dk_bar + prow * D;
-    float* vb = a.dv_bar + prow * D;
+  if (j_ok) {   // this chunk's partial sums
+    const size_t part = (size_t)chunk * a.B * a.Hkv * a.M + prow;
+    float* kb = a.dk_bar + part * D;
+    float* vb = a.dv_bar + part * D;
 #pragma unroll
     for (int nt = 0; nt < C::NOT; ++nt) {
       const int d0 = 16 * nt + 4 * lg;
@@ -661,7 +708,8 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, BLK>), dim3(8 * ((nq + 7) / 8)), dim3(4 * BLK), 0, st, a);
   if (a.approx) {
     const int tiles = (a.M + BT - 1) / BT;
-    hipLaunchKernelGGL((bwd_dtail_kernel<D, BLK>), dim3(a.B * a.Hkv * tiles), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bwd_dtail_kernel<D, BLK>), dim3(a.B * a.Hkv * tiles * kTailChunks), dim3(256), 0, st,
+                       a);
   }
   const int nk = a.B * a.Hkv * a.M;
   hipLaunchKernelGGL((bwd_dkv_kernel<D, BLK>), dim3(8 * ((nk + 7) / 8)), dim3(4 * BLK), 0, st, a);
@@ -674,11 +722,11 @@ BwdSizes bwd_sizes(const Shape& s, int approx) {
   BwdSizes z{};
   const size_t W = (size_t)(s.M + 31) / 32;
   z.lse = (size_t)s.B * s.Hq * s.N * sizeof(float);
-  z.delta = z.lse;
+  z.delta = 2 * z.lse;   // D, then L log2 e
   z.sel_bits = (size_t)s.B * s.Hq * s.M * W * sizeof(uint32_t);
   z.col_idx = (size_t)s.B * s.Hq * s.M * s.M * sizeof(int32_t);
   z.col_cnt = (size_t)s.B * s.Hkv * s.M * sizeof(int32_t);
-  z.dk_bar = approx ? (size_t)s.B * s.Hkv * s.M * s.D * sizeof(float) : 0;
+  z.dk_bar = approx ? (size_t)kTailChunks * s.B * s.Hkv * s.M * s.D * sizeof(float) : 0;
   z.dv_bar = z.dk_bar;
   return z;
 }
