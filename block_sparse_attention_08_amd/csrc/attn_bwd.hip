@@ -593,25 +593,33 @@ __global__ __launch_bounds__(4 * BLK, 2) void bwd_dkv_kernel(BwdArgs a) {
     if (tt + 1 < n_t) step(tt + 1, Q1, O1, L1, D1, Q0, O0, L0, D0);
   }
 
+  // Gradients of this block's pooled key and mean value: the sum of the
+  // pooled pass's partials, one component per thread (t < 2D), into the
+  // query buffer Q0 (free: the loop ended with a barrier).
+  const float* pooled = reinterpret_cast<const float*>(Q0);
+  if (a.approx) {
+    static_assert(4 * BLK >= 2 * D && 2 * D * 4 <= C::TB, "pooled-gradient reduction layout");
+    if (t < 2 * D) {
+      const size_t pstride = (size_t)a.B * a.Hkv * a.M * D;   // between chunks' partial sums
+      const float* src = (t < D ? a.dk_bar : a.dv_bar) + ((size_t)grp * a.M + J) * D + (t % D);
+      float sum = 0.f;
+#pragma unroll
+      for (int c = 0; c < kTailChunks; ++c) sum += src[c * pstride];
+      reinterpret_cast<float*>(Q0)[t] = sum;
+    }
+    __syncthreads();
+  }
   if (k_ok) {
     const float n = (float)min(BLK, a.N - J * BLK);
     uint16_t* kr = a.dk + krow * D;
     uint16_t* vr = a.dv + krow * D;
-    const size_t pstride = (size_t)a.B * a.Hkv * a.M * D;   // between chunks' partial sums
-    const float* kb = a.dk_bar + ((size_t)grp * a.M + J) * D;
-    const float* vb = a.dv_bar + ((size_t)grp * a.M + J) * D;
 #pragma unroll
     for (int nt = 0; nt < C::NOT; ++nt) {
       const int d0 = 16 * nt + 4 * lg;
       f32x4 x = acc.dk[nt] * a.scale, y = acc.dv[nt];
-      if (a.approx) {   // the pooled key / mean value of this block, spread over its tokens
-        f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pv = {0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < kTailChunks; ++c) {
-          pk += *reinterpret_cast<const f32x4*>(kb + c * pstride + d0);
-          pv += *reinterpret_cast<const f32x4*>(vb + c * pstride + d0);
-        }
-        x += pk / n;
-        y += pv / n;
+      if (a.approx) {   // spread evenly over the block's tokens
+        x += *reinterpret_cast<const f32x4*>(pooled + d0) / n;
+        y += *reinterpret_cast<const f32x4*>(pooled + D + d0) / n;
       }
       *reinterpret_cast<u32x2*>(kr + d0) = u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])};
       *reinterpret_cast<u32x2*>(vr + d0) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
