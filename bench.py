@@ -34,7 +34,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_F32_MFMA_TFLOPS = 157.3   # MI355X fp32 matrix peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "block-sparse attn fwd ms/layer + effective TFLOP/s (MFMA %) at N=8K–256K"
-KERNEL_SOURCES = ["pool.hip", "select.hip", "attn_bf16.hip", "attn_bf16_w16.hip", "attn_f32.hip",
+KERNEL_SOURCES = ["pool.hip", "select.hip", "attn_bf16.hip", "attn_bf16_w16.hip", "attn_f32.hip", "route_common.h",
                   "attn_common.h", "device_common.h"]
 
 

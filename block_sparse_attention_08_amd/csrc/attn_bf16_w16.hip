@@ -341,10 +341,12 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
       m = m_new;
     }
     const float mb = (m == -INFINITY ? 0.f : m) - lb;
+    // P of register pair 2tg + hp (key group tg, registers 2hp, 2hp+1) in wd;
+    // PV step cc (keys 32cc .. 32cc+31) takes slots 4cc .. 4cc+3
     uint32_t wd[8];
     float lsum = 0.f;
 #pragma unroll
-    for (int tg = 0; tg < 4; ++tg) {
+    for (int tg = 0; tg < 2; ++tg) {
 #pragma unroll
       for (int hp = 0; hp < 2; ++hp) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[tg][2 * hp], c, -mb));
@@ -353,19 +355,18 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
         lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[2 * tg + hp]), kOnes, lsum, false);
       }
     }
-    l += lsum;
-    // PV step cc (keys 32cc .. 32cc+31): slots 0-3 = key group 2cc, 4-7 = 2cc+1
-    bf16x8 pk[2];
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-      pk[cc] = __builtin_bit_cast(bf16x8, u32x4{wd[4 * cc], wd[4 * cc + 1], wd[4 * cc + 2], wd[4 * cc + 3]});
+    const bf16x8 pk0 = __builtin_bit_cast(bf16x8, u32x4{wd[0], wd[1], wd[2], wd[3]});
 
-    // ---- O^T += V^T P^T (V operands four ahead)
+    // ---- O^T += V^T P^T (V operands four ahead).  The d/16 products of
+    // keys 0..31 each carry a share of the exponentials of keys 32..63, so
+    // the matrix core and the vector ALU work side by side in this wave.
     {
       constexpr int NPV = 2 * C::NOT;
       constexpr int VD = 4;
+      constexpr int EPS = 8 / C::NOT;   // elements of keys 32..63 per product
+      static_assert(EPS * C::NOT == 8, "exponential split");
       auto vop = [&](int j) -> bf16x8 {
-        const int nt = j >> 1, cc = j & 1;
+        const int nt = j % C::NOT, cc = j / C::NOT;
         const char* p = Vs + vbase[nt] + (32 * cc) * C::ROWB;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * C::ROWB));
@@ -375,13 +376,38 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
       bf16x8 vr[VD];
 #pragma unroll
       for (int j = 0; j < VD; ++j) vr[j] = vop(j);
+      float pe = 0.f;
 #pragma unroll
-      for (int j = 0; j < NPV; ++j) {
+      for (int j = 0; j < C::NOT; ++j) {
+        const bf16x8 va = vr[j % VD];
+        vr[j % VD] = vop(j + VD);
+        o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk0, o[j], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < EPS; ++u) {
+          const int q = j * EPS + u;   // element q: key group 2 + q/4, register q%4
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[2 + (q >> 2)][q & 3], c, -mb));
+          if (q & 1) {
+            wd[4 + (q >> 1)] = pack2(pe, p);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[4 + (q >> 1)]), kOnes, lsum, false);
+            // empty volatile statements keep each value's computation in
+            // this step (plain arithmetic would be sunk to its first use)
+            asm volatile("" ::"v"(wd[4 + (q >> 1)]));
+          } else {
+            pe = p;
+            asm volatile("" ::"v"(pe));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const bf16x8 pk1 = __builtin_bit_cast(bf16x8, u32x4{wd[4], wd[5], wd[6], wd[7]});
+#pragma unroll
+      for (int j = C::NOT; j < NPV; ++j) {
         const bf16x8 va = vr[j % VD];
         if (j + VD < NPV) vr[j % VD] = vop(j + VD);
-        o[j >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[j & 1], o[j >> 1], 0, 0, 0);
+        o[j - C::NOT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk1, o[j - C::NOT], 0, 0, 0);
       }
     }
+    l += lsum;
 
     wait_vm();
     __syncthreads();   // V buffer free, K tile e+1 landed in every wave
