@@ -31,7 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
-PEAK_F32_MFMA_TFLOPS = 157.3   # MI355X fp32 matrix peak
+PEAK_F32_ALU_TFLOPS = 157.3    # MI355X fp32 vector peak (256 CUs x 2.4 GHz x 256 flop/clk)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "block-sparse attn fwd ms/layer + effective TFLOP/s (MFMA %) at N=8K–256K"
 KERNEL_SOURCES = ["pool.hip", "select.hip", "attn_bf16.hip", "attn_bf16_w16.hip", "attn_f32.hip", "route_common.h",
@@ -293,7 +293,7 @@ def main():
     sel_flops = 2.0 * wl.d * n_elig
     sel_bytes = wl.B * (wl.Hq + wl.Hkv) * M * wl.d * 4 + 4 * (int(cnt_h.sum()) + cnt_h.size)
     eff_tflops_fwd = flops / (ms_fwd * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_ALU_TFLOPS
     traffic = read_traffic(wl.name) if not args.dense else None
     eligible_blocks = n_elig
     result = {
@@ -317,7 +317,7 @@ def main():
                    "tail": bool(wl.approx and not args.dense), "parallelism": "single-gpu",
                    "routing": "fused" if args.fused_route else "pool+select"},
         "roofline": {
-            "bound": "mfma",
+            "bound": "mfma" if wl.dtype == "bf16" else "alu",
             "kernel": ("attn_f32_kernel" if wl.dtype != "bf16" else
                        "attn_w16_kernel" if wl.block == 64 else "attn_bf16_kernel"),
             "achieved": round(eff_tflops_fwd, 2), "peak": peak, "unit": "TFLOP/s",

@@ -1,11 +1,15 @@
 // Stage 3 for float32 inputs: exact attention over the listed key blocks
 // plus the 0th-order tail, on the vector ALUs in float32.
 //
-// One workgroup per (batch, head, query block), one thread per query token.
+// One workgroup (four waves) per 16 query rows of a (batch, head, query
+// block), sixteen lanes per query token (each owning D/16 of the head
+// dimension; the dot products are summed over the sixteen lanes with four
+// lane swaps).
 // Keys are visited in chunks of 64 staged in LDS; each chunk updates the
 // running max m, sum l and output o of the online softmax (FlashAttention
 // tutorial, section 2: m <- max(m, max z); l <- l e^{m_old-m} + sum e^{z-m};
-// o <- o e^{m_old-m} + sum e^{z-m} v; answer o / l).  With the tail on, each
+// o <- o e^{m_old-m} + sum e^{z-m} v; answer o / l), evaluated in base 2
+// (logits scaled by log2 e, weights 2^{z-m}: the same numbers).  With the tail on, each
 // eligible unlisted block J enters the same recurrence as one pseudo-key
 // kbar_J with weight n_J in l and value sum SigmaV_J in o (PISA explainer,
 // routing table: unselected blocks are represented by the block-mean key
@@ -18,9 +22,11 @@
 namespace sa {
 namespace {
 
-constexpr int kThreads = 128;
-constexpr int kChunk = 64;   // keys staged per LDS chunk
-constexpr int kSub = 16;     // keys per online-softmax update
+constexpr int kLanes = 16;              // lanes per query row, each owning D/16 dimensions
+constexpr int kRows = 16;               // query rows per workgroup (four waves)
+constexpr int kThreads = kLanes * kRows;
+constexpr int kChunk = 64;              // keys staged per LDS chunk
+constexpr int kSub = 16;                // keys per online-softmax update
 
 struct FwdArgs {
   const float* q;
@@ -37,19 +43,43 @@ struct FwdArgs {
   int causal, approx;
 };
 
+// Sum over the 16 lanes of a DPP row (the lanes of one query row), left in
+// every lane: quad swaps (lane ^ 1, lane ^ 2), then the half-row mirror
+// (lane i <-> 7 - i) and the row mirror (i <-> 15 - i), each pairing lanes
+// that hold disjoint partial sums.  Both lanes of a pair add the same two
+// values, so all 16 lanes end with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  static_assert(kLanes == 16, "one query row per DPP row");
+  x += dpp_mov<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  x += dpp_mov<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  x += dpp_mov<0x141>(x);   // row_half_mirror
+  x += dpp_mov<0x140>(x);   // row_mirror
+  return x;
+}
+
+// Per-thread share of one query row: dimensions [s*DL, (s+1)*DL) of q (pre-
+// scaled) and of the output accumulator; m and l are the same in all lanes
+// of a row.
 template <int D>
 struct State {
-  float q[D];
-  float o[D];
+  static constexpr int DL = D / kLanes;
+  float q[DL];
+  float o[DL];
   float m, l;
 };
 
-// Fold keys [0, n) of the staged chunk into the state.  key_pos(j) gives the
-// token index used for causal masking (or -1 for pseudo-keys), weight(j) the
-// multiplicity in l (0 masks the key out).
+// Fold keys [0, n) of the staged chunk into the state of this lane's row.
+// visible_weight(j) gives the multiplicity of key j in l (0 masks it out);
+// it is the same in all lanes of a row.  Every lane takes part (the
+// lane swaps need the whole wave); rows past the sequence end hold q = 0.
 template <int D, typename Vis>
-__device__ __forceinline__ void fold_chunk(State<D>& st, const float (*Ks)[D], const float (*Vs)[D],
-                                           int n, Vis visible_weight) {
+__device__ __forceinline__ void fold_chunk(State<D>& st, const float (*Ks)[D], const float (*Vs)[D], int n, int sl,
+                                           Vis visible_weight) {
+  constexpr int DL = State<D>::DL;
   for (int j0 = 0; j0 < n; j0 += kSub) {
     float z[kSub];
     float wgt[kSub];
@@ -58,135 +88,189 @@ __device__ __forceinline__ void fold_chunk(State<D>& st, const float (*Ks)[D], c
     for (int jj = 0; jj < kSub; ++jj) {
       const int j = j0 + jj;
       wgt[jj] = j < n ? visible_weight(j) : 0.f;
+      const float4* kr = reinterpret_cast<const float4*>(&Ks[j < n ? j : 0][sl * DL]);
       float acc = 0.f;
-      if (wgt[jj] > 0.f) {
-#pragma unroll 16
-        for (int c = 0; c < D; ++c) acc = fmaf(st.q[c], Ks[j][c], acc);
-        z[jj] = acc;
-      } else {
-        z[jj] = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < DL / 4; ++c) {
+        const float4 kv = kr[c];
+        acc = fmaf(st.q[4 * c], kv.x, acc);
+        acc = fmaf(st.q[4 * c + 1], kv.y, acc);
+        acc = fmaf(st.q[4 * c + 2], kv.z, acc);
+        acc = fmaf(st.q[4 * c + 3], kv.w, acc);
       }
+      acc = row16_sum(acc);               // the row's partial sums
+      z[jj] = wgt[jj] > 0.f ? acc : -INFINITY;
       mx = fmaxf(mx, z[jj]);
     }
     const float m_new = fmaxf(st.m, mx);
     const float ms = m_new == -INFINITY ? 0.f : m_new;
-    const float corr = expf(st.m - ms);
+    const float corr = __builtin_amdgcn_exp2f(st.m - ms);
     float p[kSub];
     float lsum = 0.f;
 #pragma unroll
     for (int jj = 0; jj < kSub; ++jj) {
-      p[jj] = wgt[jj] > 0.f ? expf(z[jj] - ms) : 0.f;
+      p[jj] = wgt[jj] > 0.f ? __builtin_amdgcn_exp2f(z[jj] - ms) : 0.f;
       lsum = fmaf(wgt[jj], p[jj], lsum);
     }
     st.l = st.l * corr + lsum;
-#pragma unroll 8
-    for (int c = 0; c < D; ++c) {
-      float acc = st.o[c] * corr;
 #pragma unroll
-      for (int jj = 0; jj < kSub; ++jj) {
-        if (j0 + jj < n) acc = fmaf(p[jj], Vs[j0 + jj][c], acc);
+    for (int c = 0; c < DL; ++c) st.o[c] *= corr;
+#pragma unroll
+    for (int jj = 0; jj < kSub; ++jj) {
+      if (j0 + jj < n) {
+        const float4* vr = reinterpret_cast<const float4*>(&Vs[j0 + jj][sl * DL]);
+#pragma unroll
+        for (int c = 0; c < DL / 4; ++c) {
+          const float4 vv = vr[c];
+          st.o[4 * c] = fmaf(p[jj], vv.x, st.o[4 * c]);
+          st.o[4 * c + 1] = fmaf(p[jj], vv.y, st.o[4 * c + 1]);
+          st.o[4 * c + 2] = fmaf(p[jj], vv.z, st.o[4 * c + 2]);
+          st.o[4 * c + 3] = fmaf(p[jj], vv.w, st.o[4 * c + 3]);
+        }
       }
-      st.o[c] = acc;
     }
     st.m = m_new;
   }
 }
 
+// One chunk of rows [0, n) of a [rows, D] float32 matrix moved through
+// registers: load() issues this thread's share of global loads (zeros past
+// row n), store() writes them to LDS.
+template <int D>
+struct ChunkRegs {
+  static constexpr int NPF = kChunk * (D / 4) / kThreads;   // float4 per thread
+  static_assert(NPF * kThreads == kChunk * (D / 4), "chunk staging layout");
+  float4 x[NPF];
+  __device__ __forceinline__ void load(const float* src, int n) {
+    const float4* s4 = reinterpret_cast<const float4*>(src);
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int u = threadIdx.x + i * kThreads;
+      x[i] = u < n * (D / 4) ? s4[u] : float4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  __device__ __forceinline__ void store(float (*dst)[D]) const {
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) reinterpret_cast<float4*>(dst[0])[threadIdx.x + i * kThreads] = x[i];
+  }
+};
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(FwdArgs a) {
-  __shared__ float Ks[kChunk][D];
-  __shared__ float Vs[kChunk][D];
+  constexpr int DL = State<D>::DL;
+  __shared__ __attribute__((aligned(16))) float Ks[kChunk][D];
+  __shared__ __attribute__((aligned(16))) float Vs[kChunk][D];
   __shared__ uint32_t selbits[kMaxBlocks / 32];
 
-  const int item = blockIdx.x;
+  const int parts = a.block / kRows;            // workgroups per query block
+  const int item = blockIdx.x / parts;
+  const int part = blockIdx.x - item * parts;
   const int bh = item / a.M;
   const int I = item - bh * a.M;
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;
   const int g = h / (a.Hq / a.Hkv);
   const int t = threadIdx.x;
-  const int qi = I * a.block + t;                 // this thread's query token
-  const bool active = t < a.block && qi < a.N;
+  const int row = t / kLanes, sl = t % kLanes;   // query row in the block, dimension slice
+  const int qi = I * a.block + part * kRows + row;   // this lane's query token
+  const bool active = qi < a.N;
   const size_t kvbase = (size_t)(b * a.Hkv + g) * a.N * D;
 
+  // logits in log2 units: q scaled by scale * log2 e, weights exp2(z - m)
+  const float qs = a.scale * 1.4426950408889634f;
   State<D> st;
   st.m = -INFINITY;
   st.l = 0.f;
+  {
+    const float4* qr = reinterpret_cast<const float4*>(a.q + ((size_t)bh * a.N + (active ? qi : 0)) * D + sl * DL);
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
-    st.q[c] = active ? a.q[((size_t)bh * a.N + qi) * D + c] * a.scale : 0.f;
-    st.o[c] = 0.f;
+    for (int c = 0; c < DL / 4; ++c) {
+      const float4 x = active ? qr[c] : float4{0.f, 0.f, 0.f, 0.f};
+      st.q[4 * c] = x.x * qs;
+      st.q[4 * c + 1] = x.y * qs;
+      st.q[4 * c + 2] = x.z * qs;
+      st.q[4 * c + 3] = x.w * qs;
+    }
+#pragma unroll
+    for (int c = 0; c < DL; ++c) st.o[c] = 0.f;
   }
 
   const int n_sel = a.cnt[(size_t)bh * a.M + I];
   const int32_t* list = a.idx + ((size_t)bh * a.M + I) * a.M;
-  for (int w = t; w < kMaxBlocks / 32; w += kThreads) selbits[w] = 0u;
+  for (int w = t; w < kMaxBlocks / 32; w += blockDim.x) selbits[w] = 0u;
   __syncthreads();
-  for (int e = t; e < n_sel; e += kThreads) {
+  for (int e = t; e < n_sel; e += blockDim.x) {
     const int J = list[e];
     atomicOr(&selbits[J >> 5], 1u << (J & 31));
   }
 
-  // ---- exact blocks
-  for (int e = 0; e < n_sel; ++e) {
-    const int J = list[e];
-    const int k0 = J * a.block;
-    const int kn = min(a.block, a.N - k0);
-    for (int c0 = 0; c0 < kn; c0 += kChunk) {
-      const int n = min(kChunk, kn - c0);
-      __syncthreads();
-      for (int u = t; u < n * D; u += kThreads) {
-        const int r = u / D, c = u - r * D;
-        Ks[r][c] = a.k[kvbase + (size_t)(k0 + c0 + r) * D + c];
-        Vs[r][c] = a.v[kvbase + (size_t)(k0 + c0 + r) * D + c];
-      }
-      __syncthreads();
-      if (active) {
-        const int first = k0 + c0;
-        const int causal = a.causal;
-        fold_chunk<D>(st, Ks, Vs, n, [&](int j) -> float {
-          return (!causal || first + j <= qi) ? 1.f : 0.f;
-        });
-      }
+  // Chunk sequence: the listed blocks (ceil(block / 64) chunks each), then,
+  // with the tail on, the pooled rows of blocks [0, Jend) in chunks of 64.
+  // Chunk ci + 1 is loaded into registers while chunk ci is folded.
+  const int per_blk = (a.block + kChunk - 1) / kChunk;
+  const int n_exact = n_sel * per_blk;
+  const int Jend = a.causal ? I + 1 : a.M;
+  const int n_chunks = n_exact + (a.approx ? (Jend + kChunk - 1) / kChunk : 0);
+  const size_t pbase = (size_t)(b * a.Hkv + g) * a.M * D;
+  // chunk ci: first row (token index, or pooled-row index for the tail) and row count
+  auto chunk_rows = [&](int ci, int& first, int& n) {
+    if (ci < n_exact) {
+      const int k0 = list[ci / per_blk] * a.block;
+      first = k0 + (ci % per_blk) * kChunk;
+      n = min(min(a.block, a.N - k0) - (ci % per_blk) * kChunk, kChunk);
+    } else {
+      first = (ci - n_exact) * kChunk;
+      n = min(kChunk, Jend - first);
     }
-  }
-
-  // ---- 0th-order tail: eligible blocks not in the list
-  if (a.approx) {
-    const int Jend = a.causal ? I + 1 : a.M;
-    const size_t pbase = (size_t)(b * a.Hkv + g) * a.M * D;
-    for (int c0 = 0; c0 < Jend; c0 += kChunk) {
-      const int n = min(kChunk, Jend - c0);
-      __syncthreads();
-      for (int u = t; u < n * D; u += kThreads) {
-        const int r = u / D, c = u - r * D;
-        Ks[r][c] = a.k_bar[pbase + (size_t)(c0 + r) * D + c];
-        Vs[r][c] = a.v_sum[pbase + (size_t)(c0 + r) * D + c];
-      }
-      __syncthreads();
-      if (active) {
-        const int M = a.M, N = a.N, blk = a.block;
-        fold_chunk<D>(st, Ks, Vs, n, [&](int j) -> float {
-          const int J = c0 + j;
-          if ((selbits[J >> 5] >> (J & 31)) & 1u) return 0.f;
-          return J == M - 1 ? (float)(N - J * blk) : (float)blk;
-        });
-      }
+  };
+  ChunkRegs<D> kr, vr;
+  auto load_chunk = [&](int ci) {
+    int first, n;
+    chunk_rows(ci, first, n);
+    if (ci < n_exact) {
+      kr.load(a.k + kvbase + (size_t)first * D, n);
+      vr.load(a.v + kvbase + (size_t)first * D, n);
+    } else {
+      kr.load(a.k_bar + pbase + (size_t)first * D, n);
+      vr.load(a.v_sum + pbase + (size_t)first * D, n);
+    }
+  };
+  if (n_chunks > 0) load_chunk(0);
+  for (int ci = 0; ci < n_chunks; ++ci) {
+    __syncthreads();                 // previous chunk folded by every wave
+    kr.store(Ks);
+    vr.store(Vs);
+    __syncthreads();
+    if (ci + 1 < n_chunks) load_chunk(ci + 1);
+    int first, n;
+    chunk_rows(ci, first, n);
+    if (ci < n_exact) {
+      const int causal = a.causal;
+      fold_chunk<D>(st, Ks, Vs, n, sl, [&](int j) -> float { return (!causal || first + j <= qi) ? 1.f : 0.f; });
+    } else {
+      // 0th-order tail: eligible blocks not in the list, weight n_J
+      const int M = a.M, N = a.N, blk = a.block;
+      fold_chunk<D>(st, Ks, Vs, n, sl, [&](int j) -> float {
+        const int J = first + j;
+        if ((selbits[J >> 5] >> (J & 31)) & 1u) return 0.f;
+        return J == M - 1 ? (float)(N - J * blk) : (float)blk;
+      });
     }
   }
 
   if (active) {
     const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
-    if (a.lse) a.lse[(size_t)bh * a.N + qi] = st.m + logf(st.l);
-    float* o = a.out + ((size_t)bh * a.N + qi) * D;
+    if (a.lse && sl == 0) a.lse[(size_t)bh * a.N + qi] = st.m * 0.6931471805599453f + logf(st.l);
+    float4* o = reinterpret_cast<float4*>(a.out + ((size_t)bh * a.N + qi) * D + sl * DL);
 #pragma unroll
-    for (int c = 0; c < D; ++c) o[c] = st.o[c] * inv;
+    for (int c = 0; c < DL / 4; ++c)
+      o[c] = float4{st.o[4 * c] * inv, st.o[4 * c + 1] * inv, st.o[4 * c + 2] * inv, st.o[4 * c + 3] * inv};
   }
 }
 
 template <int D>
 hipError_t run(const FwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((attn_f32_kernel<D>), dim3(a.total), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((attn_f32_kernel<D>), dim3(a.total * (a.block / kRows)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
