@@ -34,8 +34,13 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_F32_ALU_TFLOPS = 157.3    # MI355X fp32 vector peak (256 CUs x 2.4 GHz x 256 flop/clk)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "block-sparse attn fwd ms/layer + effective TFLOP/s (MFMA %) at N=8K–256K"
-KERNEL_SOURCES = ["pool.hip", "select.hip", "attn_bf16.hip", "attn_bf16_w16.hip", "attn_f32.hip", "route_common.h",
-                  "attn_common.h", "device_common.h"]
+# sources each attention kernel is built from (a counter summary is used only
+# while their hash matches the one it was taken on)
+KERNEL_SOURCES = {
+    "attn_w16_kernel": ["attn_bf16_w16.hip", "attn_common.h", "device_common.h", "launch.h"],
+    "attn_bf16_kernel": ["attn_bf16.hip", "attn_common.h", "device_common.h", "launch.h"],
+    "attn_f32_kernel": ["attn_f32.hip", "device_common.h", "launch.h"],
+}
 
 
 def parse():
@@ -83,17 +88,21 @@ def work_units(idx, cnt, N, block, causal, approx):
     return exact, tail
 
 
-def kernel_hash():
+def kernel_hash(kernel=None):
+    """Hash of the sources of `kernel` (a key of KERNEL_SOURCES), or of every
+    library source when None."""
+    csrc = os.path.join(ROOT, "block_sparse_attention_08_amd", "csrc")
+    files = KERNEL_SOURCES[kernel] if kernel else sorted(os.listdir(csrc))
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "block_sparse_attention_08_amd", "csrc", f), "rb") as fh:
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload):
-    """HBM bytes per attention launch from the committed counter summary, if it
-    was taken on the current kernel sources (else None)."""
+def read_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if
+    it covers that kernel and was taken on its current sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_attn_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -102,7 +111,7 @@ def read_traffic(workload):
         if "=" in line and not line.startswith("#"):
             a, b = line.split("=", 1)
             kv[a.strip()] = b.strip()
-    if kv.get("kernel_sources_sha") != kernel_hash():
+    if kv.get("kernel", "").split("<")[0] != kernel or kv.get("kernel_sources_sha") != kernel_hash(kernel):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -294,7 +303,9 @@ def main():
     sel_bytes = wl.B * (wl.Hq + wl.Hkv) * M * wl.d * 4 + 4 * (int(cnt_h.sum()) + cnt_h.size)
     eff_tflops_fwd = flops / (ms_fwd * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_ALU_TFLOPS
-    traffic = read_traffic(wl.name) if not args.dense else None
+    attn_kernel = ("attn_f32_kernel" if wl.dtype != "bf16" else
+                   "attn_w16_kernel" if wl.block == 64 else "attn_bf16_kernel")
+    traffic = read_traffic(wl.name, attn_kernel) if not args.dense else None
     eligible_blocks = n_elig
     result = {
         "metric": METRIC,
@@ -318,8 +329,7 @@ def main():
                    "routing": "fused" if args.fused_route else "pool+select"},
         "roofline": {
             "bound": "mfma" if wl.dtype == "bf16" else "alu",
-            "kernel": ("attn_f32_kernel" if wl.dtype != "bf16" else
-                       "attn_w16_kernel" if wl.block == 64 else "attn_bf16_kernel"),
+            "kernel": attn_kernel,
             "achieved": round(eff_tflops_fwd, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(eff_tflops_fwd / peak, 4),
             "traffic": traffic,
