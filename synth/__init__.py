@@ -14,5 +14,6 @@ from .workloads import (  # noqa: F401
     get_config,
     make_group,
     make_inputs,
+    output_gradient,
     random_qkv,
 )

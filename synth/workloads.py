@@ -109,7 +109,7 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
 # seeded streams
 # --------------------------------------------------------------------------
 
-_S_STRUCT, _S_KNOISE, _S_V, _S_Q0 = 0, 1, 2, 16
+_S_STRUCT, _S_KNOISE, _S_V, _S_Q0, _S_DOUT = 0, 1, 2, 16, 64
 
 
 def _rng(seed: int, tag: int, b: int, g: int, stream: int) -> np.random.Generator:
@@ -221,6 +221,16 @@ def make_inputs(wl: Workload, seed: int = 0, groups: Optional[List[int]] = None
             k[b, g] = kg
             v[b, g] = vg
     return q, k, v
+
+
+def output_gradient(wl: Workload, seed: int = 0) -> np.ndarray:
+    """Seeded dL/d(out) [B,Hq,N,d] for gradient tests: iid N(0,1) per (batch,
+    query head) from its own stream (bf16-exact for bf16 workloads)."""
+    g = np.empty((wl.B, wl.Hq, wl.N, wl.d), np.float32)
+    for b in range(wl.B):
+        for h in range(wl.Hq):
+            g[b, h] = _normal(_rng(seed, wl.tag, b, h, _S_DOUT), (wl.N, wl.d))
+    return bf16_round(g) if wl.dtype == "bf16" else g
 
 
 def random_qkv(B: int, Hq: int, Hkv: int, N: int, d: int, *, seed: int, block: int = 64,

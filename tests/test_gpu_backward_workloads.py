@@ -1,0 +1,113 @@
+"""Gradients at the workloads' full sizes, through the C ABI, in the launch
+configuration of the benchmark's backward run (pool -> select -> fwd_lse ->
+bwd over every head at once), on the GPU's own selection:
+
+* dq of a seeded sample of query blocks against the oracle's gradient of
+  that block (``attend_block_grad``, float64);
+* on the 8K image workload, dk and dv of one whole head (the oracle adds the
+  contributions of all 128 query blocks);
+* on every head, two identities that hold at any size: summed over a KV
+  head's tokens, dv equals the sum of dO over the query heads that read it
+  (each row's softmax weights, pooled blocks included, sum to one), and dk
+  sums to zero (each row of dS sums to zero).  A dropped tail, a missing
+  1/n_J spread or a sign error breaks them by far more than the tolerance.
+
+Tolerances: per compared block or head, 2e-2 * max|ref| (bf16 P and dS,
+the small-shape backward tests explain the bound); the identities within
+2e-3 of the sum of magnitudes (bf16 rounding is unbiased and averages out
+over N tokens)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import lists_to_mask, say, to_dev, to_host
+from synth import get_config, make_inputs, output_gradient
+
+pytestmark = pytest.mark.gpu
+
+REL = 2e-2
+ID_REL = 2e-3
+WORKLOADS = ["dit_image_8k", "dit_video_32k", "llm_prefill_128k_tail", "llm_prefill_256k"]
+
+
+def _run(wl, q, k, v, dout):
+    import torch
+    import block_sparse_attention_08_amd as bsa
+    desc = bsa.make_desc(wl.B, wl.Hq, wl.Hkv, wl.N, wl.d, block=wl.block, dtype=wl.dtype,
+                         alpha=wl.alpha if wl.select == "alpha" else None,
+                         density=wl.density if wl.select == "density" else None,
+                         causal=wl.causal, approx=wl.approx)
+    qd, kd, vd, gd = (to_dev(x, "bf16") for x in (q, k, v, dout))
+    ws = bsa.Workspace(desc)
+    bws = bsa.BwdWorkspace(desc)
+    bsa.block_pool(desc, qd, kd, vd, ws.q_bar, ws.k_bar, ws.v_sum, ws.tail)
+    bsa.select(desc, ws.q_bar, ws.k_bar, ws.blk_idx, ws.blk_cnt)
+    out = torch.empty_like(qd)
+    bsa.fwd_lse(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, ws.blk_idx, ws.blk_cnt, out, bws.lse)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    bsa.bwd(desc, qd, kd, vd, ws.tail, ws.blk_idx, ws.blk_cnt, out, gd, bws, dq, dk, dv)
+    torch.cuda.synchronize()
+    mask = lists_to_mask(to_host(ws.blk_idx), to_host(ws.blk_cnt))
+    return mask, to_host(dq), to_host(dk), to_host(dv)
+
+
+def _block_grad(wl, q, k, v, dout, mask, b, h, I, elig, scale):
+    g = oracle.kv_group(h, wl.Hq, wl.Hkv)
+    r0, r1 = I * wl.block, min(wl.N, (I + 1) * wl.block)
+    return oracle.attend_block_grad(q[b, h, r0:r1], r0, dout[b, h, r0:r1], k[b, g], v[b, g], mask[b, h, I],
+                                    elig[I], block=wl.block, scale=scale, causal=wl.causal, approx=wl.approx)
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_full_size_gradients(name):
+    wl = get_config(name)
+    say(f"workload {name}: generating inputs")
+    q, k, v = make_inputs(wl, seed=0)
+    dout = output_gradient(wl, seed=0)
+    say("  running pool, select, fwd_lse, bwd")
+    mask, dq, dk, dv = _run(wl, q, k, v, dout)
+    M, G = wl.M, wl.Hq // wl.Hkv
+    scale = 1.0 / np.sqrt(wl.d)
+    elig = oracle.eligible_mask(M, wl.causal)
+
+    # identities on every KV head
+    for b in range(wl.B):
+        for g in range(wl.Hkv):
+            ref = dout[b, g * G:(g + 1) * G].sum(axis=(0, 1), dtype=np.float64)
+            got = dv[b, g].sum(axis=0, dtype=np.float64)
+            mag = np.abs(dv[b, g]).sum(axis=0, dtype=np.float64)
+            assert np.all(np.abs(got - ref) <= ID_REL * mag + 1e-3), ("dv sum", b, g)
+            got = dk[b, g].sum(axis=0, dtype=np.float64)
+            mag = np.abs(dk[b, g]).sum(axis=0, dtype=np.float64)
+            assert np.all(np.abs(got) <= ID_REL * mag + 1e-3), ("dk sum", b, g)
+    say("  identities hold on every head")
+
+    # dq of sampled query blocks
+    rng = np.random.default_rng(4321)
+    picks = {(0, 0, 0), (0, wl.Hq - 1, M - 1)}
+    while len(picks) < 6:
+        picks.add((0, int(rng.integers(wl.Hq)), int(rng.integers(M))))
+    for b, h, I in sorted(picks):
+        gq, _, _ = _block_grad(wl, q, k, v, dout, mask, b, h, I, elig, scale)
+        r0 = I * wl.block
+        got = dq[b, h, r0:r0 + gq.shape[0]]
+        err, top = np.abs(got - gq).max(), np.abs(gq).max()
+        say(f"  dq (b={b}, h={h}, I={I}): max-abs err {err:.3e}, max |ref| {top:.3e}")
+        assert err <= REL * top, (b, h, I)
+
+    # dk, dv of one whole head (the 8K workload: one query head per KV head)
+    if name == "dit_image_8k":
+        b, h = 0, wl.Hq - 1
+        g = oracle.kv_group(h, wl.Hq, wl.Hkv)
+        assert G == 1
+        rk = np.zeros((wl.N, wl.d))
+        rv = np.zeros((wl.N, wl.d))
+        for I in range(M):
+            _, gk, gv = _block_grad(wl, q, k, v, dout, mask, b, h, I, elig, scale)
+            rk += gk
+            rv += gv
+        for nm, got, ref in (("dk", dk[b, g], rk), ("dv", dv[b, g], rv)):
+            err, top = np.abs(got - ref).max(), np.abs(ref).max()
+            say(f"  {nm} of head {g}: max-abs err {err:.3e}, max |ref| {top:.3e}")
+            assert err <= REL * top, nm

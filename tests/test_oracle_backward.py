@@ -127,3 +127,24 @@ def test_lse_with_tail_counts_block_multiplicity():
     z = np.asarray(q, np.float64)[0, 0] @ k[0, 0].T / np.sqrt(d)
     ref = np.log(np.exp(z).sum(-1))
     np.testing.assert_allclose(r["lse"][0, 0], ref, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("causal,approx", [(True, True), (False, True), (True, False)])
+def test_gradient_identities(causal, approx):
+    """Two identities of softmax attention that hold for any selection: the
+    value gradients of a KV head's tokens sum to the sum of dO over the query
+    heads reading it (every row's weights, pooled blocks with their
+    multiplicity included, sum to one), and the key gradients sum to zero
+    (every row of dS sums to zero).  A dropped 1/n_J spread or a lost tail
+    term breaks both."""
+    B, Hq, Hkv, N, d, block = 1, 4, 2, 200, 8, 16
+    q, k, v = random_qkv(B, Hq, Hkv, N, d, seed=26, block=block)
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    dout = np.random.default_rng(8).standard_normal(q.shape)
+    sel = _selection(q, k, v, block, causal, approx)
+    g = oracle.backward(q, k, v, dout, sel, block=block, causal=causal, approx=approx)
+    G = Hq // Hkv
+    for gg in range(Hkv):
+        np.testing.assert_allclose(g["dv"][0, gg].sum(0), dout[0, gg * G:(gg + 1) * G].sum((0, 1)),
+                                   atol=1e-12, rtol=0)
+        np.testing.assert_allclose(g["dk"][0, gg].sum(0), 0.0, atol=1e-12)
