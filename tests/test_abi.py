@@ -145,6 +145,37 @@ def test_compute_calls_reject_null_pointers_before_launch():
     assert h.sparse_attn_route(d, bad, bad, bad, bad, bad, bad, bad, bad, bad, None) == 5
 
 
+@needs_lib
+def test_backward_calls_validate_before_launch():
+    h = _lib.lib()
+    d = _desc()
+    n19 = [None] * 19
+    assert h.sparse_attn_fwd_lse(d, *([None] * 11)) == 1
+    assert h.sparse_attn_bwd(d, *n19) == 1
+    assert h.sparse_attn_bwd(_desc(dtype="f32", d=64), *n19) == 6        # bf16 only
+    assert h.sparse_attn_bwd_buffer_sizes(d, None) == 1
+    bad = ctypes.c_void_p(0x1003)
+    assert h.sparse_attn_bwd(d, *([bad] * 18), None) == 5
+    # a non-NULL forward call with a NULL lse is rejected too
+    assert h.sparse_attn_fwd_lse(d, bad, bad, bad, bad, bad, bad, bad, bad, bad, None, None) == 1
+
+
+@needs_lib
+@pytest.mark.parametrize("approx,causal", [(True, False), (False, True)])
+def test_backward_buffer_sizes(approx, causal):
+    B, Hq, Hkv, N, d, block = 2, 32, 8, 131072 - 5, 128, 128
+    M, G, W = -(-N // block), Hq // Hkv, -(-(-(-N // block)) // 32)
+    s = bsa.bwd_buffer_sizes(_desc(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, block=block, approx=approx, causal=causal,
+                                   density=None, alpha=0.5))
+    assert s["lse"] == B * Hq * N * 4
+    assert s["delta"] == 2 * B * Hq * N * 4                  # D, then lse log2 e
+    assert s["sel_bits"] == B * Hq * M * W * 4
+    assert s["col_idx"] == B * Hkv * M * G * M * 4
+    assert s["col_cnt"] == B * Hkv * M * 4
+    pooled = 16 * B * Hkv * M * d * 4 if approx else 0       # 16 partial sums per pooled row
+    assert s["dk_bar"] == pooled and s["dv_bar"] == pooled
+
+
 def test_make_desc_needs_exactly_one_rule():
     with pytest.raises(ValueError):
         bsa.make_desc(1, 1, 1, 64, 64, block=64, dtype="bf16")
