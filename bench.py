@@ -191,7 +191,7 @@ def cpu_baseline(wl, seed, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
         sys.exit(2)
     import torch
