@@ -565,7 +565,11 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
     const float mb = softmax_max<D, BLK>(st, sc, c, t0 ? log2_blk : 0.f);
     // S of tile e+1 (on the last tile this reads a retired buffer and the
     // result is dropped) interleaved with the softmax of tile e
+    // the product-dense part runs at raised wave priority; the other wave
+    // of the SIMD fills the gaps with its masks and row maxima
+    __builtin_amdgcn_s_setprio(1);
     pipe_step<D, BLK>(st, sc, sn, Kn, Vc, kbase, vbase, qf, c, mb);
+    __builtin_amdgcn_s_setprio(0);
     wait_vm();
     __syncthreads();
     t0 = t1;

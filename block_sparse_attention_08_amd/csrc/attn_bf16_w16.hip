@@ -273,6 +273,10 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
 
     // ---- S^T = K Q^T (K operands read three steps ahead)
     f32x4 s[4];
+    // the matrix phases (S, PV) run at raised wave priority: a wave that is
+    // issuing products keeps the matrix core fed while the other waves of
+    // the SIMD fill the gaps with their softmax arithmetic
+    __builtin_amdgcn_s_setprio(1);
     {
       constexpr int NSTEP = 4 * C::NKS;
       constexpr int KD = 3;
@@ -293,6 +297,7 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
         s[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], s[tg], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     wait_vm();
     __syncthreads();               // K buffer free, V tile e landed in every wave
     if (e + 1 < n_tiles) issue_k(e + 1, key1);
@@ -374,6 +379,7 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
             bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       };
       bf16x8 vr[VD];
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int j = 0; j < VD; ++j) vr[j] = vop(j);
       float pe = 0.f;
@@ -409,6 +415,7 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
     }
     l += lsum;
 
+    __builtin_amdgcn_s_setprio(0);
     wait_vm();
     __syncthreads();   // V buffer free, K tile e+1 landed in every wave
     if (e + 1 < n_tiles) issue_v(e + 1, key1);

@@ -383,8 +383,10 @@ __global__ __launch_bounds__(4 * BLK, 2) void bwd_dq_kernel(BwdArgs a) {
   __syncthreads();
   for (int e = 0; e < n_tiles; ++e) {
     f32x4 s[4], dp[4];
+    __builtin_amdgcn_s_setprio(1);
     gemm_rows<D>(s, Kt, fr, qf);
     gemm_rows<D>(dp, Vt, fr, gf);
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();                           // V tile free
     const int key1 = e + 1 < n_tiles ? tile_key(e + 1) : 0;
     if (e + 1 < n_tiles) issue(e + 1, key1, true);
@@ -424,7 +426,9 @@ __global__ __launch_bounds__(4 * BLK, 2) void bwd_dq_kernel(BwdArgs a) {
       }
     bf16x8 pk[2];
     pack_rows(s, pk);
+    __builtin_amdgcn_s_setprio(1);
     gemm_tr<D>(dq, Kt, fr, pk);                // dQ^T += K^T dS^T
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();                           // K tile free
     if (e + 1 < n_tiles) issue(e + 1, key1, false);
     wait_vm();
@@ -460,8 +464,12 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, KvAcc<D, NW, POOLED>& 
                                         const bf16x8 (&kf)[BC<D>::NKS], const bf16x8 (&vf)[BC<D>::NKS],
                                         int lg, float lw, int diag_lim) {
   f32x4 s[4], dp[4];
+  // matrix phases at raised wave priority (the other waves of the SIMD fill
+  // the gaps with their vector work)
+  __builtin_amdgcn_s_setprio(1);
   gemm_rows<D>(s, Qt, fr, kf);                 // S  = Q K^T   (rows: queries)
   gemm_rows<D>(dp, Ot, fr, vf);                // dP = dO V^T
+  __builtin_amdgcn_s_setprio(0);
   const float c = a.scale_log2;
 #pragma unroll
   for (int tg = 0; tg < 4; ++tg) {
@@ -479,8 +487,10 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, KvAcc<D, NW, POOLED>& 
   bf16x8 pk[2], dk_[2];
   pack_rows(s, pk);
   pack_rows(dp, dk_);
+  __builtin_amdgcn_s_setprio(1);
   gemm_tr<D>(acc.dv, Ot, fr, pk);              // dV^T += dO^T P
   gemm_tr<D>(acc.dk, Qt, fr, dk_);             // dK^T += Q^T dS
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Query tile (rows q0.. of head bh) into Qt/Ot, the L log2 e and D values
