@@ -47,14 +47,18 @@ hipError_t run_route(const RouteArgs& r, hipStream_t st) {
   return hipGetLastError();
 }
 
-// LDS holds the strip's keys: 8 KB (M <= 128), 33 KB (M <= 512), 131 KB
-// (M <= 2048).  Sixteen waves (one per row of the strip in the select phase)
-// where that fills the CU; eight for 129..512 blocks, where two 16-wave
-// workgroups per CU measured slower than four 8-wave ones.
+// LDS holds the strip's keys: 8 KB (M <= 128), 33 KB (M <= 512), 66 KB
+// (M <= 1024), 131 KB (M <= 2048).  Sixteen waves (one per row of the strip
+// in the select phase) where that fills the CU; eight for 129..1024 blocks,
+// where several 8-wave workgroups per CU overlap one another's load latency,
+// products and selection (measured faster than fewer 16-wave ones: at 1024
+// blocks two 8-wave workgroups per CU take 107 us against 131 us for one
+// 16-wave workgroup with the 2048-block layout).
 template <int D>
 hipError_t dispatch_route(const RouteArgs& r, hipStream_t st) {
   if (r.M <= 128) return run_route<D, 16, 2>(r, st);
   if (r.M <= 512) return run_route<D, 8, 8>(r, st);
+  if (r.M <= 1024) return run_route<D, 8, 16>(r, st);
   return run_route<D, 16, 32>(r, st);
 }
 
