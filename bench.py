@@ -313,8 +313,10 @@ def main():
     sel_bytes = wl.B * (wl.Hq + wl.Hkv) * M * wl.d * 4 + 4 * (int(cnt_h.sum()) + cnt_h.size)
     eff_tflops_fwd = flops / (ms_fwd * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_ALU_TFLOPS
+    # the library's dispatch: 64-row blocks with fewer than 384 blocks per row
+    # run the 16-row-per-wave kernel, every other bf16 case the pipelined one
     attn_kernel = ("attn_f32_kernel" if wl.dtype != "bf16" else
-                   "attn_w16_kernel" if wl.block == 64 else "attn_bf16_kernel")
+                   "attn_w16_kernel" if wl.block == 64 and M < 384 else "attn_bf16_kernel")
     traffic = read_traffic(wl.name, attn_kernel) if not args.dense else None
     eligible_blocks = n_elig
     result = {

@@ -46,9 +46,12 @@
 // last tail tile) are visited last, so the main loop carries no mask code;
 // the order of the tiles does not change the softmax.
 // 128-row blocks: four waves, 64-key tiles, 64 KB of tile buffers, two
-// workgroups per CU.  (The template also builds 64-row blocks as two waves
-// over 32-key tiles; measured slower than the 16-row-per-wave kernel on the
-// 8K image workload, faster on the 32K video one, it is not dispatched.)
+// workgroups per CU.  64-row blocks with at least kPipelinedMinBlocks64
+// blocks per row: two waves over 32-key tiles (32 KB of tile buffers, four
+// workgroups per CU); measured against the 16-row-per-wave kernel on the
+// image workload's inputs: 10% slower at 192 blocks, even at 384, 17% faster
+// at 512 and 27% at 640, where the double-buffered tiles hide K/V fetches
+// that no longer hit in the caches.
 // Workgroups are ordered so that each XCD receives a contiguous range of
 // (kv head, query block) items, with the query heads of one KV group
 // adjacent, so K/V blocks shared by neighbouring items stay in one L2.
@@ -69,6 +72,9 @@ hipError_t launch_fwd_w16(const Shape& s, const FwdParams& p, const void* q, con
                           const int32_t* blk_cnt, void* out, hipStream_t st);
 
 namespace {
+
+// 64-row blocks per row from which the pipelined two-wave kernel is used
+constexpr int kPipelinedMinBlocks64 = 384;
 
 struct FwdArgs {
   const uint16_t* q;
@@ -620,8 +626,12 @@ hipError_t launch_fwd(const Shape& s, const FwdParams& p, const void* q, const v
                       const int32_t* blk_idx, const int32_t* blk_cnt, void* out, hipStream_t st) {
   if (s.dtype == 0)
     return launch_fwd_f32(s, p, q, k, v, k_bar, v_sum, blk_idx, blk_cnt, out, st);
-  // 64-row query blocks: 16 rows per wave (four waves share one K/V tile)
-  if (s.block == 64) return launch_fwd_w16(s, p, q, k, v, tail, blk_idx, blk_cnt, out, st);
+  // 64-row query blocks up to 383 blocks per row: 16 rows per wave (four
+  // waves share one K/V tile, four workgroups per CU); longer rows take the
+  // two-wave pipelined kernel below, whose double-buffered tiles hide the
+  // longer K/V fetches once a head's K/V outgrows the caches
+  if (s.block == 64 && s.M < kPipelinedMinBlocks64)
+    return launch_fwd_w16(s, p, q, k, v, tail, blk_idx, blk_cnt, out, st);
   FwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -643,6 +653,7 @@ hipError_t launch_fwd(const Shape& s, const FwdParams& p, const void* q, const v
   a.scale_log2 = p.scale * 1.4426950408889634f;
   a.causal = p.causal;
   a.approx = p.approx;
+  if (s.block == 64) return s.D == 128 ? run<128, 64>(a, st) : run<64, 64>(a, st);
   return s.D == 128 ? run<128, 128>(a, st) : run<64, 128>(a, st);
 }
 

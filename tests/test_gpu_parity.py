@@ -25,6 +25,9 @@ CASES = [
     (2, 2, 1, 700, 64, 64, "bf16", True, True, "alpha"),         # causal + tail (forced diagonal)
     (1, 4, 2, 2600, 128, 128, "bf16", True, True, "alpha"),     # causal + tail, 128-row blocks, GQA
     (1, 2, 2, 900, 64, 128, "bf16", False, False, "density"),
+    # 64-row blocks with >= 384 blocks per row take the pipelined two-wave kernel
+    (1, 2, 2, 24616, 128, 64, "bf16", False, True, "density"),   # M = 385, ragged 384*64 + 40
+    (1, 2, 1, 24600, 64, 64, "bf16", True, True, "alpha"),       # d = 64, causal + tail, GQA
     (1, 2, 2, 640, 64, 64, "f32", False, True, "alpha"),
     (1, 2, 1, 555, 128, 128, "f32", True, False, "density"),
     (1, 3, 3, 777, 128, 64, "f32", True, True, "density"),
@@ -169,3 +172,29 @@ def test_deterministic_and_stream_ordered():
         c = int(c0[pos])
         assert torch.equal(i0[pos][:c], i1[pos][:c])
     assert torch.equal(o0, o1)
+
+
+def test_lse_of_both_64_row_kernels():
+    """fwd_lse on 64-row blocks below and above the two-wave kernel's
+    threshold (M = 128 and 385): out and lse against the oracle on its own
+    lists."""
+    import torch
+    import block_sparse_attention_08_amd as bsa
+    for N in (8192 + 17, 24616):
+        q, k, v = random_qkv(1, 2, 2, N, 128, seed=12, block=64, dtype="bf16", kind="cluster", noise=0.5)
+        ref = oracle.forward(q, k, v, block=64, causal=False, approx=True, mode="density", density=0.2)
+        desc = bsa.make_desc(1, 2, 2, N, 128, block=64, dtype="bf16", density=0.2, approx=True)
+        qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
+        ws = bsa.Workspace(desc)
+        bsa.block_pool(desc, qd, kd, vd, ws.q_bar, ws.k_bar, ws.v_sum, ws.tail)
+        idx, cnt = oracle.mask_to_lists(ref["mask"])
+        out = torch.empty_like(qd)
+        lse = torch.empty((1, 2, N), dtype=torch.float32, device="cuda")
+        bsa.fwd_lse(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, torch.from_numpy(idx).cuda(),
+                    torch.from_numpy(cnt).cuda(), out, lse)
+        torch.cuda.synchronize()
+        err_o = np.abs(to_host(out) - ref["out"]).max()
+        err_l = np.abs(to_host(lse) - ref["lse"]).max()
+        say(f"  N={N}: out err {err_o:.3e}, lse err {err_l:.3e}")
+        assert err_o <= TOL_OUT["bf16"]
+        assert err_l <= 2e-3 * (1 + np.abs(ref["lse"]).max())
