@@ -210,8 +210,15 @@ def block_sparse_attention(q, k, v, *, block_size: int = 64, alpha: Optional[flo
         workspace = Workspace(desc, device=q.device)
     ws = workspace
     desc = ws.desc
+    want_dt = SA_DTYPE_BF16 if q.dtype == torch.bfloat16 else SA_DTYPE_F32
+    if (tuple(q.shape) != (desc.batch, desc.heads_q, desc.seq_len, desc.head_dim)
+            or k.shape[1] != desc.heads_kv or desc.dtype != want_dt or ws.q_bar.device != q.device):
+        raise ValueError("workspace was built for another shape, dtype or device")
     if out is None:
         out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor of q's shape, dtype and device")
     block_pool(desc, q, k, v, ws.q_bar, ws.k_bar, ws.v_sum, ws.tail)
     select(desc, ws.q_bar, ws.k_bar, ws.blk_idx, ws.blk_cnt)
     fwd(desc, q, k, v, ws.k_bar, ws.v_sum, ws.tail, ws.blk_idx, ws.blk_cnt, out)

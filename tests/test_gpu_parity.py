@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import TOL_OUT, assert_pool, compare_masks, run_gpu, say, to_dev, to_host
+from gpu_helpers import TOL_OUT, assert_pool, compare_masks, lists_to_mask, run_gpu, say, to_dev, to_host
 from synth import random_qkv
 
 pytestmark = pytest.mark.gpu
@@ -198,3 +198,28 @@ def test_lse_of_both_64_row_kernels():
         say(f"  N={N}: out err {err_o:.3e}, lse err {err_l:.3e}")
         assert err_o <= TOL_OUT["bf16"]
         assert err_l <= 2e-3 * (1 + np.abs(ref["lse"]).max())
+
+
+def test_wrapper_rejects_mismatched_workspace_and_out():
+    """The Python wrapper refuses a workspace built for another shape and an
+    out tensor unlike q (the library itself only sees raw pointers)."""
+    import torch
+    import block_sparse_attention_08_amd as bsa
+    q, k, v = random_qkv(1, 2, 2, 256, 64, seed=9, block=64, dtype="bf16")
+    qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
+    other = bsa.Workspace(bsa.make_desc(1, 2, 2, 512, 64, block=64, dtype="bf16", density=0.2))
+    with pytest.raises(ValueError):
+        bsa.block_sparse_attention(qd, kd, vd, density=0.2, workspace=other)
+    with pytest.raises(ValueError):
+        bsa.block_sparse_attention(qd, kd, vd, density=0.2,
+                                   out=torch.empty((1, 2, 256, 32), dtype=torch.bfloat16, device="cuda"))
+    ws = bsa.Workspace(bsa.make_desc(1, 2, 2, 256, 64, block=64, dtype="bf16", density=0.2))
+    out = torch.empty_like(qd)
+    o = bsa.block_sparse_attention(qd, kd, vd, density=0.2, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == out.data_ptr()
+    gpu_mask = lists_to_mask(to_host(ws.blk_idx), to_host(ws.blk_cnt))
+    assert (gpu_mask.sum(-1) == oracle.topk_count(4, 0.2)).all()
+    ref = oracle.forward(q, k, v, block=64, causal=False, approx=True, mode="density", density=0.2,
+                         sel=gpu_mask)
+    assert np.abs(to_host(o) - ref["out"]).max() <= TOL_OUT["bf16"]
