@@ -21,16 +21,18 @@
 //   bwd_bitmap  the selection as bits, one row per (batch, query head, block)
 //   bwd_cols    per (batch, KV group, key block J): the (query head, query
 //               block) pairs that list J, ascending (the transposed lists)
-//   bwd_dq      per query block, like the forward: its listed blocks, then
-//               its unlisted eligible pooled rows (gathered), tile by tile:
-//               S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T
+//   bwd_dq      per 64 query rows of a query block, like the forward: its
+//               listed blocks, then its unlisted eligible pooled rows
+//               (gathered), tile by tile: S^T = K Q^T, dP^T = V dO^T, dS^T,
+//               dQ^T += K^T dS^T
 //   bwd_dtail   per KV group, 64 pooled rows and one of 16 ranges of query
 //               blocks: every query block of the range whose tail holds
 //               them: S = Q Kbar^T, dP = dO Vbar^T, dVbar^T += dO^T P,
 //               dKbar^T += Q^T dS (float32 partial sums per range)
-//   bwd_dkv     per key block: the pairs of its transposed list, tile by tile,
-//               dV^T += dO^T P, dK^T += Q^T dS; adds the pooled gradients
-//               of its block (the 16 partial sums) / n_J and writes dk, dv
+//   bwd_dkv     per 64 keys of a key block: the pairs of its transposed
+//               list, tile by tile, dV^T += dO^T P, dK^T += Q^T dS; adds the
+//               pooled gradients of its block (the 16 partial sums) / n_J
+//               and writes dk, dv
 // All products are v_mfma_f32_16x16x32_bf16 with 16 rows (queries, keys or
 // pooled rows) per wave held in registers and 64-row tiles of the other
 // operand in LDS (HBM -> LDS by buffer loads into LDS).  One XOR swizzle of
@@ -261,9 +263,12 @@ __global__ __launch_bounds__(64) void bwd_cols_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dq
+// Workgroup per 64 query rows (four waves): a 128-row block is split over two
+// workgroups, adjacent in the item order so they share its K/V tiles in L2.
 template <int D, int BLK>
-__global__ __launch_bounds__(4 * BLK, 2) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int NW = BLK / 16;
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int NW = 4;
+  constexpr int PARTS = BLK / 64;              // 64-row parts of a block
   constexpr int NT = 64 * NW;
   constexpr int SUB = BLK / BT;                // 64-key tiles per block
   using C = BC<D>;
@@ -273,11 +278,12 @@ __global__ __launch_bounds__(4 * BLK, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ uint32_t selbits[kMaxBlocks / 32];
   __shared__ uint16_t tail_rows[kMaxBlocks];
 
-  const int total = a.B * a.Hq * a.M;
+  const int total = a.B * a.Hq * a.M * PARTS;
   const int item = xcd_local_item(blockIdx.x, total);
   if (item < 0) return;
-  const int hg = item % a.G;
-  int rest = item / a.G;
+  const int part = item % PARTS;
+  const int hg = (item / PARTS) % a.G;
+  int rest = item / PARTS / a.G;
   const int I = a.M - 1 - rest % a.M;
   rest /= a.M;
   const int g = rest % a.Hkv;
@@ -289,7 +295,7 @@ __global__ __launch_bounds__(4 * BLK, 2) void bwd_dq_kernel(BwdArgs a) {
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int q_tok = I * BLK + 16 * w + lr;
+  const int q_tok = I * BLK + 64 * part + 16 * w + lr;
   const bool q_ok = q_tok < a.N;
   const size_t qrow = (size_t)bh * a.N + (q_ok ? q_tok : 0);
 
@@ -513,9 +519,13 @@ __device__ __forceinline__ void issue_query_tile(const BwdArgs& a, int bh, int q
   }
 }
 
+// Workgroup per 64 keys (four waves): a 128-row block is split over two
+// workgroups, adjacent in the item order so they share its query tiles in L2
+// (two independent workgroups per CU hide each other's barriers).
 template <int D, int BLK>
-__global__ __launch_bounds__(4 * BLK, 2) void bwd_dkv_kernel(BwdArgs a) {
-  constexpr int NW = BLK / 16;
+__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
+  constexpr int NW = 4;
+  constexpr int PARTS = BLK / 64;              // 64-key parts of a block
   constexpr int SUB = BLK / BT;
   using C = BC<D>;
   using DM = Dma<D, NW>;
@@ -530,11 +540,13 @@ __global__ __launch_bounds__(4 * BLK, 2) void bwd_dkv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float D0[BT];
   __shared__ __attribute__((aligned(16))) float D1[BT];
 
-  const int total = a.B * a.Hkv * a.M;
+  const int total = a.B * a.Hkv * a.M * PARTS;
   const int item = xcd_local_item(blockIdx.x, total);
   if (item < 0) return;
-  const int grp = item / a.M;                  // b * Hkv + g
-  const int J = item - grp * a.M;
+  const int part = item % PARTS;
+  const int blk = item / PARTS;
+  const int grp = blk / a.M;                   // b * Hkv + g
+  const int J = blk - grp * a.M;
   const int b = grp / a.Hkv;
   const int g = grp - b * a.Hkv;
 
@@ -542,7 +554,7 @@ __global__ __launch_bounds__(4 * BLK, 2) void bwd_dkv_kernel(BwdArgs a) {
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int k_tok = J * BLK + 16 * w + lr;
+  const int k_tok = J * BLK + 64 * part + 16 * w + lr;
   const bool k_ok = k_tok < a.N;
   const size_t krow = (size_t)grp * a.N + (k_ok ? k_tok : 0);
   bf16x8 kf[C::NKS], vf[C::NKS];
@@ -608,7 +620,7 @@ __global__ __launch_bounds__(4 * BLK, 2) void bwd_dkv_kernel(BwdArgs a) {
   // query buffer Q0 (free: the loop ended with a barrier).
   const float* pooled = reinterpret_cast<const float*>(Q0);
   if (a.approx) {
-    static_assert(4 * BLK >= 2 * D && 2 * D * 4 <= C::TB, "pooled-gradient reduction layout");
+    static_assert(64 * NW >= 2 * D && 2 * D * 4 <= C::TB, "pooled-gradient reduction layout");
     if (t < 2 * D) {
       const size_t pstride = (size_t)a.B * a.Hkv * a.M * D;   // between chunks' partial sums
       const float* src = (t < D ? a.dk_bar : a.dv_bar) + ((size_t)grp * a.M + J) * D + (t % D);
@@ -722,15 +734,15 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, st, a);
   hipLaunchKernelGGL(bwd_bitmap_kernel, dim3(a.B * a.Hq * a.M), dim3(64), 0, st, a);
   hipLaunchKernelGGL(bwd_cols_kernel, dim3(a.B * a.Hkv * a.W), dim3(64), 0, st, a);
-  const int nq = a.B * a.Hq * a.M;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, BLK>), dim3(8 * ((nq + 7) / 8)), dim3(4 * BLK), 0, st, a);
+  const int nq = a.B * a.Hq * a.M * (BLK / 64);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BLK>), dim3(8 * ((nq + 7) / 8)), dim3(256), 0, st, a);
   if (a.approx) {
     const int tiles = (a.M + BT - 1) / BT;
     hipLaunchKernelGGL((bwd_dtail_kernel<D, BLK>), dim3(a.B * a.Hkv * tiles * kTailChunks), dim3(256), 0, st,
                        a);
   }
-  const int nk = a.B * a.Hkv * a.M;
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, BLK>), dim3(8 * ((nk + 7) / 8)), dim3(4 * BLK), 0, st, a);
+  const int nk = a.B * a.Hkv * a.M * (BLK / 64);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, BLK>), dim3(8 * ((nk + 7) / 8)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
