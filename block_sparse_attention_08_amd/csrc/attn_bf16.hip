@@ -557,6 +557,8 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
   __syncthreads();
   f32x16 sA[C::NJS], sB[C::NJS];
   qk_tile<D, BLK>(sA, K0, kbase, qf);
+  // every wave has read tile 0 from K0 before step 0 loads tile 2 into it
+  __syncthreads();
 
   // one tile step; Kn holds tile e+1 (read now) and receives tile e+2, Vc
   // holds tile e, Vn receives tile e+1; sc is S of tile e, sn receives S of
