@@ -223,3 +223,50 @@ def test_wrapper_rejects_mismatched_workspace_and_out():
     ref = oracle.forward(q, k, v, block=64, causal=False, approx=True, mode="density", density=0.2,
                          sel=gpu_mask)
     assert np.abs(to_host(o) - ref["out"]).max() <= TOL_OUT["bf16"]
+
+
+@pytest.mark.parametrize("N,block,causal,mode", [(4096 + 17, 64, False, "density"), (4096 + 100, 128, True, "alpha")])
+def test_graph_capture_replays_match_eager(N, block, causal, mode):
+    """pool -> select -> fwd captured in a HIP graph (torch.cuda.CUDAGraph):
+    three replays, with eager work on the buffers in between, each give the
+    eager run's lists and outputs bit for bit (the library records no memset
+    or allocation, so the captured launches are the whole computation)."""
+    import torch
+    import block_sparse_attention_08_amd as bsa
+    q, k, v = random_qkv(1, 4, 2, N, 128, seed=13, block=block, dtype="bf16", kind="cluster", noise=0.5)
+    qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
+    desc = bsa.make_desc(1, 4, 2, N, 128, block=block, dtype="bf16", alpha=0.5 if mode == "alpha" else None,
+                         density=0.2 if mode == "density" else None, causal=causal, approx=True)
+    ws = bsa.Workspace(desc)
+    out = torch.empty_like(qd)
+
+    def layer():
+        bsa.block_pool(desc, qd, kd, vd, ws.q_bar, ws.k_bar, ws.v_sum, ws.tail)
+        bsa.select(desc, ws.q_bar, ws.k_bar, ws.blk_idx, ws.blk_cnt)
+        bsa.fwd(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, ws.blk_idx, ws.blk_cnt, out)
+
+    layer()
+    torch.cuda.synchronize()
+    ref_out, ref_cnt, ref_idx = out.clone(), ws.blk_cnt.clone(), ws.blk_idx.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    cnt_h = to_host(ref_cnt)
+    for rep in range(3):
+        out.zero_()
+        ws.blk_cnt.zero_()
+        ws.k_bar.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {rep}")
+        assert torch.equal(out, ref_out), rep
+        assert torch.equal(ws.blk_cnt, ref_cnt), rep
+        idx, ridx = to_host(ws.blk_idx), to_host(ref_idx)
+        for pos in np.ndindex(*cnt_h.shape):
+            c = int(cnt_h[pos])
+            assert np.array_equal(idx[pos][:c], ridx[pos][:c]), (rep, pos)
