@@ -61,6 +61,8 @@ def parse():
                    help="attend every eligible block (caller lists), the dense comparison run")
     p.add_argument("--backward", action="store_true",
                    help="also run the gradients (fwd_lse + bwd) each step and report them")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the HIP-graph replay of the step (reported beside the eager figures)")
     p.add_argument("--fused-route", action="store_true",
                    help="pool + select in one cooperative launch (sparse_attn_route)")
     return p.parse_args()
@@ -296,6 +298,28 @@ def main():
     ms_step = wall * 1e3 / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
 
+    # The same step captured once in a HIP graph and replayed K times (the
+    # launch gaps between the stages go away); reported beside the eager
+    # figures, which stay the bench line.
+    graph_ms = None
+    if not (args.no_graph or args.fused_route or args.backward or args.dense):
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        print(f"[bench] graph replay: {graph_ms:.3f} ms/step", file=sys.stderr, flush=True)
+
     # algorithmic work of this selection
     if args.dense:
         idx_h, cnt_h = dense_idx.cpu().numpy(), dense_cnt.cpu().numpy()
@@ -361,6 +385,11 @@ def main():
                                         * (0.5 if wl.causal else 1.0) / (ms_step * 1e-3) / 1e12, 2),
         },
     }
+    if graph_ms is not None:
+        result["graph"] = {
+            "ms_per_step": round(graph_ms, 4), "value": round(flops / (graph_ms * 1e-3) / 1e12, 3),
+            "note": "the same step captured in a HIP graph and replayed; value, ms_per_step and the "
+                    "stages above come from the eager steps"}
     if args.backward:
         ms_bwd = np.mean([e[3].elapsed_time(e[4]) for e in evs])
         bflops = 10.0 * wl.d * (ex + tl)      # S, dP, dV, dK, dQ: 2d each per pair
