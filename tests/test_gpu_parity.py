@@ -174,30 +174,31 @@ def test_deterministic_and_stream_ordered():
     assert torch.equal(o0, o1)
 
 
-def test_lse_of_both_64_row_kernels():
-    """fwd_lse on 64-row blocks below and above the two-wave kernel's
-    threshold (M = 128 and 385): out and lse against the oracle on its own
-    lists."""
+@pytest.mark.parametrize("N,dtype,causal", [(8192 + 17, "bf16", False), (24616, "bf16", False),
+                                             (1000, "f32", False), (777, "f32", True)])
+def test_lse_of_each_forward_kernel(N, dtype, causal):
+    """fwd_lse through each forward kernel that serves 64-row blocks (the
+    16-row bf16 kernel at M = 129, the pipelined one at M = 385, the float32
+    one): out and lse against the oracle on its own lists."""
     import torch
     import block_sparse_attention_08_amd as bsa
-    for N in (8192 + 17, 24616):
-        q, k, v = random_qkv(1, 2, 2, N, 128, seed=12, block=64, dtype="bf16", kind="cluster", noise=0.5)
-        ref = oracle.forward(q, k, v, block=64, causal=False, approx=True, mode="density", density=0.2)
-        desc = bsa.make_desc(1, 2, 2, N, 128, block=64, dtype="bf16", density=0.2, approx=True)
-        qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
-        ws = bsa.Workspace(desc)
-        bsa.block_pool(desc, qd, kd, vd, ws.q_bar, ws.k_bar, ws.v_sum, ws.tail)
-        idx, cnt = oracle.mask_to_lists(ref["mask"])
-        out = torch.empty_like(qd)
-        lse = torch.empty((1, 2, N), dtype=torch.float32, device="cuda")
-        bsa.fwd_lse(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, torch.from_numpy(idx).cuda(),
-                    torch.from_numpy(cnt).cuda(), out, lse)
-        torch.cuda.synchronize()
-        err_o = np.abs(to_host(out) - ref["out"]).max()
-        err_l = np.abs(to_host(lse) - ref["lse"]).max()
-        say(f"  N={N}: out err {err_o:.3e}, lse err {err_l:.3e}")
-        assert err_o <= TOL_OUT["bf16"]
-        assert err_l <= 2e-3 * (1 + np.abs(ref["lse"]).max())
+    q, k, v = random_qkv(1, 2, 2, N, 128, seed=12, block=64, dtype=dtype, kind="cluster", noise=0.5)
+    ref = oracle.forward(q, k, v, block=64, causal=causal, approx=True, mode="density", density=0.2)
+    desc = bsa.make_desc(1, 2, 2, N, 128, block=64, dtype=dtype, density=0.2, approx=True, causal=causal)
+    qd, kd, vd = (to_dev(x, dtype) for x in (q, k, v))
+    ws = bsa.Workspace(desc)
+    bsa.block_pool(desc, qd, kd, vd, ws.q_bar, ws.k_bar, ws.v_sum, ws.tail)
+    idx, cnt = oracle.mask_to_lists(ref["mask"])
+    out = torch.empty_like(qd)
+    lse = torch.empty((1, 2, N), dtype=torch.float32, device="cuda")
+    bsa.fwd_lse(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, torch.from_numpy(idx).cuda(),
+                torch.from_numpy(cnt).cuda(), out, lse)
+    torch.cuda.synchronize()
+    err_o = np.abs(to_host(out) - ref["out"]).max()
+    err_l = np.abs(to_host(lse) - ref["lse"]).max()
+    say(f"  N={N} {dtype}: out err {err_o:.3e}, lse err {err_l:.3e}")
+    assert err_o <= TOL_OUT[dtype]
+    assert err_l <= (2e-3 if dtype == "bf16" else 1e-5) * (1 + np.abs(ref["lse"]).max())
 
 
 def test_wrapper_rejects_mismatched_workspace_and_out():
