@@ -57,6 +57,8 @@
 // adjacent, so K/V blocks shared by neighbouring items stay in one L2.
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn_common.h"
 #include "device_common.h"
 #include "launch.h"
@@ -563,13 +565,16 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
   // one tile step; Kn holds tile e+1 (read now) and receives tile e+2, Vc
   // holds tile e, Vn receives tile e+1; sc is S of tile e, sn receives S of
   // tile e+1
+  // tile step; masked: whether the tile may be one of the last (masked) ones
   auto step = [&](int e, const char* Kn, char* Kc, const char* Vc, char* Vn, f32x16 (&sc)[C::NJS],
-                  f32x16 (&sn)[C::NJS]) __attribute__((always_inline)) {
+                  f32x16 (&sn)[C::NJS], auto masked) __attribute__((always_inline)) {
     int k2 = 0;
     const bool t2 = e + 2 < n_tiles ? tile_src(e + 2, k2) : false;
     if (e + 1 < n_tiles) issue_v(t1, k1, Vn);
     if (e + 2 < n_tiles) issue_k(t2, k2, Kc);
-    if (e >= P2) mask_tile(sc, t0, k0);   // the last tiles only
+    if constexpr (decltype(masked)::value) {
+      if (e >= P2) mask_tile(sc, t0, k0);
+    }
     const float mb = softmax_max<D, BLK>(st, sc, c, t0 ? log2_blk : 0.f);
     // S of tile e+1 (on the last tile this reads a retired buffer and the
     // result is dropped) interleaved with the softmax of tile e
@@ -585,11 +590,20 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
     t1 = t2;
     k1 = k2;
   };
+  // Tiles before P2 need no mask.  Their loop has no mask branch, so the S
+  // accumulators of both phases stay in fixed registers (a branch that
+  // rewrites them would cost a copy of S per tile at its join).
   int e = 0;
+  while (e + 1 < P2) {
+    step(e, K1, K0, V0, V1, sA, sB, std::false_type{});
+    step(e + 1, K0, K1, V1, V0, sB, sA, std::false_type{});
+    e += 2;
+  }
+  // the last tiles (the masked ones among them); e is even here
   while (e < n_tiles) {
-    step(e, K1, K0, V0, V1, sA, sB);
+    step(e, K1, K0, V0, V1, sA, sB, std::true_type{});
     if (++e >= n_tiles) break;
-    step(e, K0, K1, V1, V0, sB, sA);
+    step(e, K0, K1, V1, V0, sB, sA, std::true_type{});
     ++e;
   }
 
