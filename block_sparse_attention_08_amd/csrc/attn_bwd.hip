@@ -17,7 +17,7 @@
 // sparse_attn_fwd_lse) gives P without a running max: exp2(z log2 e - L log2 e).
 //
 // Kernels (one launch each, in order):
-//   bwd_delta   D_i = dO_i . o_i and L_i log2 e (float32)
+//   bwd_delta   D_i = dO_i . o_i and -L_i log2 e (float32)
 //   bwd_bitmap  the selection as bits, one row per (batch, query head, block)
 //   bwd_cols    per (batch, KV group, key block J): the (query head, query
 //               block) pairs that list J, ascending (the transposed lists)
@@ -205,7 +205,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, LPR);
   if (row < rows && c == 0) {
     a.delta[row] = acc;
-    a.delta[rows + row] = a.lse[row] * kLog2e;   // log-denominator in log2 units
+    // minus the log-denominator in log2 units: the exponent of P is then
+    // one fused multiply-add of the score
+    a.delta[rows + row] = -a.lse[row] * kLog2e;
   }
 }
 
@@ -302,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   bf16x8 qf[C::NKS], gf[C::NKS];
   load_row<D>(qf, a.q + qrow * D, q_ok, lg);
   load_row<D>(gf, a.dout + qrow * D, q_ok, lg);
-  const float Lc = q_ok ? a.delta[(size_t)a.B * a.Hq * a.N + qrow] : INFINITY;   // P = 0 on padding rows
+  const float nLc = q_ok ? a.delta[(size_t)a.B * a.Hq * a.N + qrow] : -INFINITY;   // P = 0 on padding rows
   const float Dd = q_ok ? a.delta[qrow] : 0.f;
 
   const int n_sel = scalar_view(a.cnt)[(size_t)bh * a.M + I];
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         for (int r = 0; r < 4; ++r) s[tg][r] = 16 * tg + r < lim ? s[tg][r] : -INFINITY;
     }
     // P = exp2(z log2 e + lb - L log2 e), dS = P (dP - D)
-    const float off = lb - Lc;
+    const float off = lb + nLc;
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg)
 #pragma unroll
@@ -466,9 +468,9 @@ struct KvAcc {
 
 template <int D, int NW, bool POOLED>
 __device__ __forceinline__ void kv_tile(const BwdArgs& a, KvAcc<D, NW, POOLED>& acc, const char* Qt, const char* Ot,
-                                        const float* Lt, const float* Dt, const Frag<D>& fr,
+                                        const float* nLt, const float* Dt, const Frag<D>& fr,
                                         const bf16x8 (&kf)[BC<D>::NKS], const bf16x8 (&vf)[BC<D>::NKS],
-                                        int lg, float lw, int diag_lim) {
+                                        int lg, float lw, bool diag, int diag_lim) {
   f32x4 s[4], dp[4];
   // matrix phases at raised wave priority (the other waves of the SIMD fill
   // the gaps with their vector work)
@@ -477,15 +479,22 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, KvAcc<D, NW, POOLED>& 
   gemm_rows<D>(dp, Ot, fr, vf);                // dP = dO V^T
   __builtin_amdgcn_s_setprio(0);
   const float c = a.scale_log2;
+  // causal diagonal (a tile of the key block's own query block, the same
+  // for the whole workgroup): query row 16tg + 4lg + r sees the key only at
+  // or after it
+  if (!POOLED && diag) {
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[tg][r] = 16 * tg + 4 * lg + r >= diag_lim ? s[tg][r] : -INFINITY;
+  }
 #pragma unroll
   for (int tg = 0; tg < 4; ++tg) {
-    const f32x4 L = *reinterpret_cast<const f32x4*>(Lt + 16 * tg + 4 * lg);
+    const f32x4 nL = *reinterpret_cast<const f32x4*>(nLt + 16 * tg + 4 * lg);
     const f32x4 Dv = *reinterpret_cast<const f32x4*>(Dt + 16 * tg + 4 * lg);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float p = __builtin_amdgcn_exp2f(fmaf(s[tg][r], c, lw - L[r]));
-      // causal diagonal: query row (16tg + 4lg + r) sees the key only at or after it
-      if (!POOLED) p = 16 * tg + 4 * lg + r >= diag_lim ? p : 0.f;
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[tg][r], c, POOLED ? lw + nL[r] : nL[r]));
       s[tg][r] = p;
       dp[tg][r] = p * (dp[tg][r] - Dv[r]);
     }
@@ -499,7 +508,7 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, KvAcc<D, NW, POOLED>& 
   __builtin_amdgcn_s_setprio(0);
 }
 
-// Query tile (rows q0.. of head bh) into Qt/Ot, the L log2 e and D values
+// Query tile (rows q0.. of head bh) into Qt/Ot, the -L log2 e and D values
 // of its rows into Lt/Dt, all by loads into LDS (waves 0 and 1 move the 64
 // floats).  Rows past the end of the sequence read zeros: Q and dO rows of
 // zero make P dO, dP and D zero there, so such rows add nothing.
@@ -529,7 +538,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int SUB = BLK / BT;
   using C = BC<D>;
   using DM = Dma<D, NW>;
-  // double-buffered query tiles (Q, dO, and the L, D of their rows), each
+  // double-buffered query tiles (Q, dO, and the -L log2 e, D of their rows), each
   // buffer a separate LDS object named statically in the unrolled loop
   __shared__ __attribute__((aligned(1024))) char Q0[C::TB];
   __shared__ __attribute__((aligned(1024))) char Q1[C::TB];
@@ -602,8 +611,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
     }
     // causal diagonal: row r of the tile (token q0 + r) sees key k_tok iff
     // r >= k_tok - q0
-    const int diag_lim = (a.causal && I0 == J) ? k_tok - q00 : -BT;
-    kv_tile<D, NW, false>(a, acc, Qc, Oc, Lc, Dc, fr, kf, vf, lg, 0.f, diag_lim);
+    kv_tile<D, NW, false>(a, acc, Qc, Oc, Lc, Dc, fr, kf, vf, lg, 0.f, a.causal && I0 == J, k_tok - q00);
     wait_vm();
     __syncthreads();
     bh0 = bh1;
@@ -710,7 +718,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dtail_kernel(BwdArgs a) {
         issue_query_tile<D, NW>(a, bh, q0, Qt, Ot, Lt, Dt, w, voff);
         wait_vm();
         __syncthreads();
-        kv_tile<D, NW, true>(a, acc, Qt, Ot, Lt, Dt, fr, kf, vf, lg, lw, 0);
+        kv_tile<D, NW, true>(a, acc, Qt, Ot, Lt, Dt, fr, kf, vf, lg, lw, false, 0);
         __syncthreads();
       }
     }
@@ -752,7 +760,7 @@ BwdSizes bwd_sizes(const Shape& s, int approx) {
   BwdSizes z{};
   const size_t W = (size_t)(s.M + 31) / 32;
   z.lse = (size_t)s.B * s.Hq * s.N * sizeof(float);
-  z.delta = 2 * z.lse;   // D, then L log2 e
+  z.delta = 2 * z.lse;   // D, then -L log2 e
   z.sel_bits = (size_t)s.B * s.Hq * s.M * W * sizeof(uint32_t);
   z.col_idx = (size_t)s.B * s.Hq * s.M * s.M * sizeof(int32_t);
   z.col_cnt = (size_t)s.B * s.Hkv * s.M * sizeof(int32_t);

@@ -187,7 +187,7 @@ sa_status sparse_attn_fwd_lse(const sa_desc* desc, const void* q, const void* k,
 
 typedef struct {        /* bytes of the backward's caller-allocated buffers */
   size_t lse;           /* [B, Hq, N] float32 (written by sparse_attn_fwd_lse)          */
-  size_t delta;         /* 2 x [B, Hq, N] float32 scratch: dO . o, then lse log2 e      */
+  size_t delta;         /* 2 x [B, Hq, N] float32 scratch: dO . o, then -lse log2 e     */
   size_t sel_bits;      /* [B, Hq, M, ceil(M/32)] uint32 scratch: the selection as bits */
   size_t col_idx;       /* [B, Hkv, M, (Hq/Hkv)*M] int32 scratch: transposed lists      */
   size_t col_cnt;       /* [B, Hkv, M] int32 scratch                                     */

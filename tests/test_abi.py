@@ -168,7 +168,7 @@ def test_backward_buffer_sizes(approx, causal):
     s = bsa.bwd_buffer_sizes(_desc(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, block=block, approx=approx, causal=causal,
                                    density=None, alpha=0.5))
     assert s["lse"] == B * Hq * N * 4
-    assert s["delta"] == 2 * B * Hq * N * 4                  # D, then lse log2 e
+    assert s["delta"] == 2 * B * Hq * N * 4                  # D, then -lse log2 e
     assert s["sel_bits"] == B * Hq * M * W * 4
     assert s["col_idx"] == B * Hkv * M * G * M * 4
     assert s["col_cnt"] == B * Hkv * M * 4
