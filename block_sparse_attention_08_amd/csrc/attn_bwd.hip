@@ -113,6 +113,87 @@ struct Frag {
   }
 };
 
+// LDS fragments are read this many products ahead of the product that uses
+// them, through a ring of registers.
+constexpr int kRing = 6;
+
+// Two row products, interleaved step by step:
+//   acc0[tg] = T0_rows(16tg..16tg+15) . R0^T,  acc1[tg] = T1_rows(..) . R1^T
+// lane (lr, lg), register r = tile row 16tg + 4lg + r against register row
+// lr.  A scheduling barrier after each product keeps the program order: the
+// read kRing steps ahead is issued before each product, so the products run
+// back to back while the later reads are in flight, and products on one
+// accumulator are eight steps apart.
+template <int D>
+__device__ __forceinline__ void gemm_rows2(f32x4 (&acc0)[4], const char* t0, const bf16x8 (&r0)[BC<D>::NKS],
+                                           f32x4 (&acc1)[4], const char* t1, const bf16x8 (&r1)[BC<D>::NKS],
+                                           const Frag<D>& f) {
+  constexpr int NS = 2 * 4 * BC<D>::NKS;     // tiles x row groups x d steps
+  // step i: tile i & 1, row group (i >> 1) % 4, d step (i >> 1) / 4
+  auto frag = [&](int i) -> bf16x8 {
+    const char* t = (i & 1) ? t1 : t0;
+    return *reinterpret_cast<const bf16x8*>(t + f.rb[(i >> 1) / 4] + 16 * ((i >> 1) % 4) * BC<D>::ROWB);
+  };
+#pragma unroll
+  for (int tg = 0; tg < 4; ++tg) {
+    acc0[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc1[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8 ring[kRing];
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) ring[i] = frag(i);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const bf16x8 a = ring[i % kRing];
+    if (i + kRing < NS) ring[i % kRing] = frag(i + kRing);
+    const int tg = (i >> 1) % 4, st = (i >> 1) / 4;
+    if (i & 1)
+      acc1[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, r1[st], acc1[tg], 0, 0, 0);
+    else
+      acc0[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, r0[st], acc0[tg], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Transposed fragment of d-tile nt, tile rows 32cc .. 32cc + 31.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, const Frag<D>& f, int nt, int cc) {
+  const char* p = tile + f.tb[nt] + 32 * cc * BC<D>::ROWB;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * BC<D>::ROWB));
+  return __builtin_bit_cast(
+      bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
+// Two transposed products, interleaved step by step:
+//   acc0[nt] += T0^T(d-tile nt) . X0,  acc1[nt] += T1^T(d-tile nt) . X1,
+// X packed from a gemm_rows-shaped array (x[cc]: tile rows of row groups 2cc
+// and 2cc+1).  Read ring and scheduling as in gemm_rows2; products on one
+// accumulator are 2 * (d tiles) steps apart.
+template <int D>
+__device__ __forceinline__ void gemm_tr2(f32x4 (&acc0)[BC<D>::NOT], const char* t0, const bf16x8 (&x0)[2],
+                                         f32x4 (&acc1)[BC<D>::NOT], const char* t1, const bf16x8 (&x1)[2],
+                                         const Frag<D>& f) {
+  constexpr int NOT = BC<D>::NOT;
+  constexpr int NS = 2 * 2 * NOT;            // tiles x halves x d tiles
+  // step i: tile i & 1, d tile (i >> 1) % NOT, half (i >> 1) / NOT
+  auto frag = [&](int i) -> bf16x8 { return tr_frag<D>((i & 1) ? t1 : t0, f, (i >> 1) % NOT, (i >> 1) / NOT); };
+  bf16x8 ring[kRing];
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) ring[i] = frag(i);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const bf16x8 a = ring[i % kRing];
+    if (i + kRing < NS) ring[i % kRing] = frag(i + kRing);
+    const int nt = (i >> 1) % NOT, cc = (i >> 1) / NOT;
+    if (i & 1)
+      acc1[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, x1[cc], acc1[nt], 0, 0, 0);
+    else
+      acc0[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, x0[cc], acc0[nt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // acc[tg] = T_rows(16tg..16tg+15) . R^T: lane (lr, lg), register r = tile row
 // 16tg + 4lg + r against register row lr.
 template <int D>
@@ -475,8 +556,18 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, KvAcc<D, NW, POOLED>& 
   // matrix phases at raised wave priority (the other waves of the SIMD fill
   // the gaps with their vector work)
   __builtin_amdgcn_s_setprio(1);
-  gemm_rows<D>(s, Qt, fr, kf);                 // S  = Q K^T   (rows: queries)
-  gemm_rows<D>(dp, Ot, fr, vf);                // dP = dO V^T
+  // dk/dv: the products read their LDS operands through the read-ahead
+  // ring (two waves per SIMD leave LDS latency exposed otherwise; 6% faster
+  // at 128K).  The pooled pass (three waves per SIMD) and the dq pass (four)
+  // measured faster with the compiler's own schedule, which needs fewer
+  // registers.
+  constexpr bool RING = !POOLED;
+  if constexpr (RING) {
+    gemm_rows2<D>(s, Qt, kf, dp, Ot, vf, fr);   // S = Q K^T, dP = dO V^T (rows: queries)
+  } else {
+    gemm_rows<D>(s, Qt, fr, kf);
+    gemm_rows<D>(dp, Ot, fr, vf);
+  }
   __builtin_amdgcn_s_setprio(0);
   const float c = a.scale_log2;
   // causal diagonal (a tile of the key block's own query block, the same
@@ -503,8 +594,12 @@ __device__ __forceinline__ void kv_tile(const BwdArgs& a, KvAcc<D, NW, POOLED>& 
   pack_rows(s, pk);
   pack_rows(dp, dk_);
   __builtin_amdgcn_s_setprio(1);
-  gemm_tr<D>(acc.dv, Ot, fr, pk);              // dV^T += dO^T P
-  gemm_tr<D>(acc.dk, Qt, fr, dk_);             // dK^T += Q^T dS
+  if constexpr (RING) {
+    gemm_tr2<D>(acc.dv, Ot, pk, acc.dk, Qt, dk_, fr);   // dV^T += dO^T P, dK^T += Q^T dS
+  } else {
+    gemm_tr<D>(acc.dv, Ot, fr, pk);
+    gemm_tr<D>(acc.dk, Qt, fr, dk_);
+  }
   __builtin_amdgcn_s_setprio(0);
 }
 
