@@ -90,6 +90,25 @@ def work_units(idx, cnt, N, block, causal, approx):
     return exact, tail
 
 
+def lds_operand_bytes(cnt, block, d, causal, approx, kernel):
+    """Bytes the attention kernel's waves read from LDS as product operands in
+    one launch: every wave of a workgroup reads the whole K tile and the whole
+    V tile (T keys x d, bf16) of every tile the workgroup visits -- the listed
+    blocks (block / T tiles each) and the tail tiles (T pooled rows each).
+    None for kernels without LDS operand tiles."""
+    if kernel == "attn_w16_kernel":
+        nw, t = 4, 64
+    elif kernel == "attn_bf16_kernel":
+        nw, t = block // 32, block // 2
+    else:
+        return None
+    M = cnt.shape[-1]
+    jend = np.arange(1, M + 1) if causal else np.full(M, M)
+    rest = (jend - cnt.astype(np.int64)) if approx else np.zeros_like(cnt, dtype=np.int64)
+    tiles = (block // t) * cnt.astype(np.int64) + (rest + t - 1) // t
+    return float(tiles.sum()) * nw * 2 * t * d * 2
+
+
 def kernel_hash(kernel=None):
     """Hash of the sources of `kernel` (a key of KERNEL_SOURCES), or of every
     library source when None."""
@@ -121,11 +140,12 @@ def read_traffic(workload, kernel):
         return None
 
 
-def achievable_peaks(dev, read_mib=2048, reps=5, mfma_iters=20000):
-    """Rates the machine reaches with the two measurement kernels of
-    libsa_peaks.so: a streaming read of a buffer 8x the last-level cache and a
-    loop of independent bf16 matrix-core products, timed with events on the
-    launch stream."""
+def achievable_peaks(dev, read_mib=2048, reps=5, mfma_iters=20000, lds_iters=20000):
+    """Rates the machine reaches with the measurement kernels of
+    libsa_peaks.so: a streaming read of a buffer 8x the last-level cache, a
+    loop of independent bf16 matrix-core products and a loop of 16-byte LDS
+    reads, timed with events on the launch stream.  Returns HBM GB/s, MFMA
+    TFLOP/s and LDS GB/s per compute unit."""
     import ctypes
     import torch
     from block_sparse_attention_08_amd import _lib
@@ -151,8 +171,11 @@ def achievable_peaks(dev, read_mib=2048, reps=5, mfma_iters=20000):
                                           st.cuda_stream, ctypes.byref(got)))
     t_mfma = timed(lambda: h.sa_peak_mfma_bf16(mfma_iters, sink.data_ptr(), st.cuda_stream,
                                                ctypes.byref(flops)))
+    lds = ctypes.c_double(0.0)
+    t_lds = timed(lambda: h.sa_peak_lds_read(lds_iters, sink.data_ptr(), st.cuda_stream, ctypes.byref(lds)))
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     del buf
-    return got.value / t_read / 1e9, flops.value / t_mfma / 1e12
+    return got.value / t_read / 1e9, flops.value / t_mfma / 1e12, lds.value / t_lds / 1e9 / cus
 
 
 def cpu_baseline(wl, seed, budget_s):
@@ -399,11 +422,18 @@ def main():
             "frac_of_bf16_peak": round(bflops / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "note": "step = pool + select + fwd_lse + bwd; value/ms_per_step include the backward"}
     if not args.no_peaks:
-        print("[bench] measuring achievable HBM read and bf16 MFMA rates", file=sys.stderr, flush=True)
-        hbm, mfma = achievable_peaks(dev)
+        print("[bench] measuring achievable HBM read, bf16 MFMA and LDS read rates", file=sys.stderr, flush=True)
+        hbm, mfma, lds = achievable_peaks(dev)
         pool_gbps = pool_bytes / (ms_pool * 1e-3) / 1e9
+        lds_bytes = (lds_operand_bytes(cnt_h, wl.block, wl.d, wl.causal, wl.approx and not args.dense,
+                                       attn_kernel) if wl.dtype == "bf16" else None)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        fwd_lds = lds_bytes / (ms_fwd * 1e-3) / 1e9 / cus if lds_bytes else None
         result["achievable"] = {
             "hbm_read_GBps": round(hbm, 1), "mfma_bf16_TFLOPs": round(mfma, 1),
+            "lds_read_GBps_per_CU": round(lds, 1),
+            "fwd_lds_operand_GBps_per_CU": round(fwd_lds, 1) if fwd_lds else None,
+            "fwd_frac_of_achievable_lds": round(fwd_lds / lds, 4) if fwd_lds else None,
             "pool_frac_of_achievable_hbm": round(pool_gbps / hbm, 4),
             "pool_select_frac_of_achievable_hbm": round(
                 (pool_bytes + sel_bytes) / ((ms_pool + ms_sel) * 1e-3) / 1e9 / hbm, 4),

@@ -1,7 +1,8 @@
 // Achievable-rate kernels for the roofline denominators, measured on the
 // machine at hand next to the datasheet peaks: a streaming read over a buffer
-// much larger than the last-level cache (HBM), and a loop of independent bf16
-// matrix-core products (MFMA).  Measurement only; nothing on the attention
+// much larger than the last-level cache (HBM), a loop of independent bf16
+// matrix-core products (MFMA), and a loop of 16-byte LDS reads (the operand
+// path of the attention kernels).  Measurement only; nothing on the attention
 // path calls them.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -66,6 +67,33 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(int iters, float seed, u
   if (s == 1234.5f) sink[blockIdx.x & 255] = __float_as_uint(s);
 }
 
+// LDS read rate: four 256-thread workgroups per CU, each filling 32 KB of
+// LDS once, then per trip 16 ds_read_b128 per wave (1 KB each, contiguous
+// per instruction, so free of bank conflicts) kept in flight together; an
+// empty volatile statement takes every loaded vector, so no read can be
+// dropped, and a compiler memory barrier per trip keeps the reads inside
+// the loop.  Indexes stay below kLdsVec: base + 64*15 + 63 <= 1024 + 1023.
+constexpr int kLdsVec = 2048;                  // 16-byte vectors per workgroup (32 KB)
+constexpr int kLdsReads = 16;                  // reads per wave and trip
+
+__global__ __launch_bounds__(kThreads) void lds_kernel(int iters, uint32_t* sink) {
+  __shared__ u32x4 buf[kLdsVec];
+  for (int i = threadIdx.x; i < kLdsVec; i += kThreads)
+    buf[i] = u32x4{(uint32_t)i, (uint32_t)i + 1u, (uint32_t)i + 2u, (uint32_t)i + 3u};
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  for (int it = 0; it < iters; ++it) {
+    const int base = (it & 1) * (kLdsVec / 2);
+    u32x4 x[kLdsReads];
+#pragma unroll
+    for (int u = 0; u < kLdsReads; ++u) x[u] = buf[base + 64 * u + lane];
+#pragma unroll
+    for (int u = 0; u < kLdsReads; u += 4) asm volatile("" ::"v"(x[u]), "v"(x[u + 1]), "v"(x[u + 2]), "v"(x[u + 3]));
+    asm volatile("" ::: "memory");
+  }
+  if (iters < 0) sink[blockIdx.x & 255] = 1u;
+}
+
 int grid_for(int per_cu) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -96,5 +124,14 @@ SA_PEAKS_EXPORT int sa_peak_mfma_bf16(int iters, void* sink, void* stream, doubl
   *flops = (double)grid * (kThreads / 64) * (double)iters * kChains * kFlopsPerMfma;
   hipLaunchKernelGGL(mfma_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, iters, 1.0e-3f,
                      (uint32_t*)sink);
+  return (int)hipGetLastError();
+}
+
+SA_PEAKS_EXPORT int sa_peak_lds_read(int iters, void* sink, void* stream, double* bytes) {
+  if (!sink || !bytes || iters < 1) return (int)hipErrorInvalidValue;
+  const int grid = grid_for(4);
+  if (grid <= 0) return (int)hipErrorInvalidDevice;
+  *bytes = (double)grid * kThreads * (double)iters * kLdsReads * 16.0;
+  hipLaunchKernelGGL(lds_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, iters, (uint32_t*)sink);
   return (int)hipGetLastError();
 }

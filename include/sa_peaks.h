@@ -2,12 +2,13 @@
  * libsparse_attn.so.
  *
  * A roofline fraction is quoted twice: against the datasheet peak (HBM3E
- * 8 TB/s, dense bf16 matrix 2.5 PFLOP/s) and against what these two kernels
- * reach on the machine they run on.  Neither function is on the attention
- * path.
+ * 8 TB/s, dense bf16 matrix 2.5 PFLOP/s) and against what these kernels
+ * reach on the machine they run on; the LDS read rate has no datasheet
+ * figure here and sets how far the attention kernels' operand reads can
+ * keep up with their products.  No function is on the attention path.
  *
- * Both launch asynchronously on `stream` (a hipStream_t, NULL = the default
- * stream); the caller times them with events on that stream.  Both return a
+ * All launch asynchronously on `stream` (a hipStream_t, NULL = the default
+ * stream); the caller times them with events on that stream.  All return a
  * hipError_t value as int: 0 on success, hipErrorInvalidValue (1) for a NULL
  * pointer, a misaligned buffer or iters < 1, otherwise the launch error.
  * Nothing is allocated, freed or synchronised.
@@ -37,6 +38,13 @@ SA_PEAKS_EXPORT int sa_peak_read(const void* buf, size_t bytes, void* sink, void
  * the algorithmic flop count of the launch (32*32*16*2 per product).  `sink`
  * as above. */
 SA_PEAKS_EXPORT int sa_peak_mfma_bf16(int iters, void* sink, void* stream, double* flops);
+
+/* Run `iters` rounds of sixteen 16-byte LDS reads per lane (ds_read_b128,
+ * bank-conflict free, all in flight together) on four 256-thread workgroups
+ * per compute unit, each reading its own 32 KB of LDS; *bytes receives the
+ * bytes read by the launch.  Divide by the time and the compute unit count
+ * for the per-CU rate.  `sink` as above. */
+SA_PEAKS_EXPORT int sa_peak_lds_read(int iters, void* sink, void* stream, double* bytes);
 
 #ifdef __cplusplus
 }

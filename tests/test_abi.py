@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 def test_peaks_library_exports_and_rejects_bad_arguments():
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "sa_peaks.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(sa_peak_\w+)\s*\(", text)))
-    assert names == ["sa_peak_mfma_bf16", "sa_peak_read"]
+    assert names == ["sa_peak_lds_read", "sa_peak_mfma_bf16", "sa_peak_read"]
     h = _lib.peaks_lib()
     for n in names:
         assert hasattr(h, n), n
@@ -58,6 +58,8 @@ def test_peaks_library_exports_and_rejects_bad_arguments():
     assert h.sa_peak_read(None, 1 << 20, None, None, ctypes.byref(got)) == 1
     fl = ctypes.c_double(0.0)
     assert h.sa_peak_mfma_bf16(0, ctypes.c_void_p(16), None, ctypes.byref(fl)) == 1
+    assert h.sa_peak_lds_read(0, ctypes.c_void_p(16), None, ctypes.byref(fl)) == 1
+    assert h.sa_peak_lds_read(4, None, None, ctypes.byref(fl)) == 1
 
 
 @needs_lib
