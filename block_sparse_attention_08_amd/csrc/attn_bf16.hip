@@ -213,20 +213,26 @@ __device__ __forceinline__ bf16x8 k_operand(const char* Ks, const int (&kbase)[C
   return *reinterpret_cast<const bf16x8*>(Ks + kbase[ks] + 32 * js * C::ROWB);
 }
 
-// Online softmax, part 1, for one tile (S^T accumulators, already masked):
-// running max with lazy rescale of O and l.  lb is added to every logit of
-// the tile (log2 n_J for tail rows).  Returns the reference max minus lb (lb
-// while no key has been seen) for the exponentials.
+// Row max of one tile's raw scores (S^T accumulators, already masked),
+// over both lane halves.
 template <int D, int BLK>
-__device__ __forceinline__ float softmax_max(State<D, BLK>& st, const SAcc<D, BLK>& s, float c,
-                                             float lb) {
+__device__ __forceinline__ float tile_max(const SAcc<D, BLK>& s) {
   using C = Cfg<D, BLK>;
   float mx = -INFINITY;
 #pragma unroll
   for (int js = 0; js < C::NJS; ++js)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[js][r]);
-  mx = half_max(mx);
+  return half_max(mx);
+}
+
+// Online softmax, part 1, for one tile whose raw row max is mx: running max
+// with lazy rescale of O and l.  lb is added to every logit of the tile
+// (log2 n_J for tail rows).  Returns the reference max minus lb (lb while no
+// key has been seen) for the exponentials.
+template <int D, int BLK>
+__device__ __forceinline__ float softmax_update(State<D, BLK>& st, float mx, float c, float lb) {
+  using C = Cfg<D, BLK>;
   const float mxs = fmaf(mx, c, lb);
   const bool grow = mxs > st.m + 8.f;
   if (__ballot(grow)) {
@@ -271,12 +277,17 @@ __device__ __forceinline__ void qk_tile(SAcc<D, BLK>& s, const char* Ks,
 // barrier between steps keeps the compiler from regrouping the
 // exponentials ahead of the products, so the matrix cores and the vector
 // ALUs work side by side.
-template <int D, int BLK>
+// NEXT_MAX: the row max of the next tile's scores (unmasked) is folded into
+// the PV products' steps, one or two vector max operations beside each
+// product, and returned in mx_next; the vector ALU has nothing else to do
+// while those products run.
+template <int D, int BLK, bool NEXT_MAX>
 __device__ __forceinline__ void pipe_step(State<D, BLK>& st, const SAcc<D, BLK>& s,
                                           SAcc<D, BLK>& s_next, const char* Ks_next,
                                           const char* Vs, const int (&kbase)[Cfg<D, BLK>::NKS],
                                           const int (&vbase)[Cfg<D, BLK>::NOT],
-                                          const bf16x8 (&qf)[Cfg<D, BLK>::NKS], float c, float mb) {
+                                          const bf16x8 (&qf)[Cfg<D, BLK>::NKS], float c, float mb,
+                                          float& mx_next) {
   using C = Cfg<D, BLK>;
   constexpr int NSTEP = C::NJS * C::NKS;     // S MFMAs of one tile
   constexpr int NPAIR = 8 * C::NJS;          // element pairs (two scores) per lane and tile
@@ -326,12 +337,26 @@ __device__ __forceinline__ void pipe_step(State<D, BLK>& st, const SAcc<D, BLK>&
     const int base = 8 * (kc >> 1) + 4 * (kc & 1);
     pk[kc] = __builtin_bit_cast(bf16x8, u32x4{wd[base], wd[base + 1], wd[base + 2], wd[base + 3]});
   }
+  constexpr int NE = 16 * C::NJS;             // scores per lane of the next tile
+  constexpr int PE = (NE + NPV - 1) / NPV;    // of them folded per PV product
+  float mn = -INFINITY;
 #pragma unroll
   for (int j = 0; j < NPV; ++j) {
     const bf16x8 va = vr[j % VD];
     if (j + VD < NPV) vr[j % VD] = v_operand<D, BLK>(Vs, vbase, (j + VD) / NKC, (j + VD) % NKC);
     st.o[j / NKC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[j % NKC], st.o[j / NKC], 0, 0, 0);
+    if constexpr (NEXT_MAX) {
+      // scores in accumulation order: key group 0 finishes first
+#pragma unroll
+      for (int u = 0; u < PE; ++u) {
+        const int q = j * PE + u;
+        if (q < NE) mn = fmaxf(mn, s_next[q / 16][q % 16]);
+      }
+      asm volatile("" ::"v"(mn));   // keeps the max inside this step
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+  if constexpr (NEXT_MAX) mx_next = half_max(mn);
 }
 
 template <int D, int BLK>
@@ -561,6 +586,9 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
   qk_tile<D, BLK>(sA, K0, kbase, qf);
   // every wave has read tile 0 from K0 before step 0 loads tile 2 into it
   __syncthreads();
+  // raw row max of the current tile: in the unmasked loop each step
+  // computes the next tile's beside its PV products
+  float mxc = tile_max<D, BLK>(sA);
 
   // one tile step; Kn holds tile e+1 (read now) and receives tile e+2, Vc
   // holds tile e, Vn receives tile e+1; sc is S of tile e, sn receives S of
@@ -572,16 +600,18 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
     const bool t2 = e + 2 < n_tiles ? tile_src(e + 2, k2) : false;
     if (e + 1 < n_tiles) issue_v(t1, k1, Vn);
     if (e + 2 < n_tiles) issue_k(t2, k2, Kc);
-    if constexpr (decltype(masked)::value) {
+    constexpr bool MASKED = decltype(masked)::value;
+    if constexpr (MASKED) {
       if (e >= P2) mask_tile(sc, t0, k0);
+      mxc = tile_max<D, BLK>(sc);
     }
-    const float mb = softmax_max<D, BLK>(st, sc, c, t0 ? log2_blk : 0.f);
+    const float mb = softmax_update<D, BLK>(st, mxc, c, t0 ? log2_blk : 0.f);
     // S of tile e+1 (on the last tile this reads a retired buffer and the
     // result is dropped) interleaved with the softmax of tile e
     // the product-dense part runs at raised wave priority; the other wave
     // of the SIMD fills the gaps with its masks and row maxima
     __builtin_amdgcn_s_setprio(1);
-    pipe_step<D, BLK>(st, sc, sn, Kn, Vc, kbase, vbase, qf, c, mb);
+    pipe_step<D, BLK, !MASKED>(st, sc, sn, Kn, Vc, kbase, vbase, qf, c, mb, mxc);
     __builtin_amdgcn_s_setprio(0);
     wait_vm();
     __syncthreads();
