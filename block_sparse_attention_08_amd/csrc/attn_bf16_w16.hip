@@ -270,9 +270,14 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
   // PV of tile e, V e+1 during S of tile e+1.
   auto step = [&](int e, int key0, int key1, auto mode) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode)::value;
+    constexpr bool FOLD = MODE == kModePlain || MODE == kModeTail;   // tiles without masks
 
-    // ---- S^T = K Q^T (K operands read three steps ahead)
+    // ---- S^T = K Q^T (K operands read three steps ahead).  Tiles without
+    // masks fold each finished key group into the row max two products into
+    // the next group, beside the products (pinned there by scheduling
+    // barriers).
     f32x4 s[4];
+    float mx = -INFINITY;
     // the matrix phases (S, PV) run at raised wave priority: a wave that is
     // issuing products keeps the matrix core fed while the other waves of
     // the SIMD fill the gaps with their softmax arithmetic
@@ -295,6 +300,18 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
           kr[st % KD] = *reinterpret_cast<const bf16x8*>(Ks + kbase[n2 % C::NKS] + 16 * (n2 / C::NKS) * C::ROWB);
         }
         s[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[ks], s[tg], 0, 0, 0);
+        if constexpr (FOLD) {
+          if (tg > 0 && ks == (C::NKS > 2 ? 2 : C::NKS - 1)) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[tg - 1][r]);
+            asm volatile("" ::"v"(mx));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[3][r]);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -326,11 +343,12 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
     }
 
     // ---- online softmax
-    float mx = -INFINITY;
+    if constexpr (!FOLD) {
 #pragma unroll
-    for (int tg = 0; tg < 4; ++tg)
+      for (int tg = 0; tg < 4; ++tg)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[tg][r]);
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[tg][r]);
+    }
     mx = row_max4(mx);
     // tail rows: + log2(n_J) (a uniform offset; a short last block's
     // difference is already in its score)
