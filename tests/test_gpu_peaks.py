@@ -1,0 +1,30 @@
+"""GPU: the achievable-rate probes of libsa_peaks.so (measurement only) launch,
+report the work they did, and give rates in a sane range on an MI355X: the
+streaming read below the 8 TB/s datasheet figure, the bf16 product loop below
+2.5 PFLOP/s, the LDS reads near or below 256 bytes a clock per CU at
+2.4 GHz.  Short
+runs (small buffer, few iterations): the rates are checked for plausibility,
+not measured."""
+
+import math
+
+import pytest
+
+import bench
+from gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_peak_probes_report_plausible_rates():
+    import torch
+    dev = torch.device("cuda", 0)
+    say("peaks probes: read 512 MiB, 2000 product rounds, 2000 LDS rounds")
+    hbm, mfma, lds = bench.achievable_peaks(dev, read_mib=512, reps=2, mfma_iters=2000, lds_iters=2000)
+    for x in (hbm, mfma, lds):
+        assert math.isfinite(x) and x > 0.0
+    # upper bounds from the datasheet (a 512 MiB buffer may partly hit the
+    # last-level cache, so only the product and LDS rates get lower bounds)
+    assert mfma < 2500.0 and mfma > 500.0
+    assert lds < 1.1 * 256 * 2.4 and lds > 100.0
+    assert hbm < 20000.0
