@@ -1,10 +1,9 @@
 """GPU: the achievable-rate probes of libsa_peaks.so (measurement only) launch,
 report the work they did, and give rates in a sane range on an MI355X: the
-streaming read below the 8 TB/s datasheet figure, the bf16 product loop below
-2.5 PFLOP/s, the LDS reads near or below 256 bytes a clock per CU at
-2.4 GHz.  Short
-runs (small buffer, few iterations): the rates are checked for plausibility,
-not measured."""
+bf16 product loop below the 2.5 PFLOP/s datasheet figure, the LDS reads near
+or below 256 bytes a clock per CU at 2.4 GHz, the streaming read finite (a
+512 MiB buffer partly hits the 256 MB last-level cache).  Short runs: the
+rates are checked for plausibility, not measured."""
 
 import math
 
