@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -109,15 +110,24 @@ def lds_operand_bytes(cnt, block, d, causal, approx, kernel):
     return float(tiles.sum()) * nw * 2 * t * d * 2
 
 
+def _code_only(text):
+    """Source text without comments and blank lines: what the compiler sees
+    of it (no string literal in these sources holds a comment marker)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_hash(kernel=None):
-    """Hash of the sources of `kernel` (a key of KERNEL_SOURCES), or of every
-    library source when None."""
+    """Hash of the code (comments dropped) of the sources of `kernel` (a key
+    of KERNEL_SOURCES), or of every library source when None: a summary of
+    counters stays valid across edits of comments only."""
     csrc = os.path.join(ROOT, "block_sparse_attention_08_amd", "csrc")
     files = KERNEL_SOURCES[kernel] if kernel else sorted(os.listdir(csrc))
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -41,10 +41,11 @@
 // unlisted eligible blocks, built in LDS at the start.
 //
 // K and V are double-buffered and the loop is software-pipelined: S of tile
-// e+1 sits next to the softmax of tile e, one barrier per tile.  Tiles that
-// need masks (the ragged last block, the causal diagonal, the partly filled
-// last tail tile) are visited last, so the main loop carries no mask code;
-// the order of the tiles does not change the softmax.
+// e+1 sits next to the exponentials of tile e, and the row max of tile e+1
+// next to the PV products of tile e; one barrier per tile.  Tiles that need
+// masks (the ragged last block, the causal diagonal, the partly filled last
+// tail tile) are visited last, in a loop of their own, so the main loop
+// carries no mask code; the order of the tiles does not change the softmax.
 // 128-row blocks: four waves, 64-key tiles, 64 KB of tile buffers, two
 // workgroups per CU.  64-row blocks with at least kPipelinedMinBlocks64
 // blocks per row: two waves over 32-key tiles (32 KB of tile buffers, four

@@ -14,7 +14,9 @@
 //   S^T = K Q^T: 4 key groups x d/32 steps of 16x16x32 (K from LDS as A,
 //       the wave's Q rows in registers as B).  Lane l holds query row l%16,
 //       keys 16t + 4*(l/16) + r of key group t: a row's 64 scores sit in
-//       the four lanes l%16 + 16g, combined with two permlane swaps.
+//       the four lanes l%16 + 16g, combined with two permlane swaps; on
+//       tiles without masks each finished key group is folded into the row
+//       max beside the products of the next.
 //   P = exp2(S * scale * log2 e - m), packed to bf16: the registers of key
 //       groups 2c and 2c+1 are directly the B operand of PV step c.
 //   O^T += V^T P^T: d/16 tiles x 2 steps; V^T gathered from the row-major V
