@@ -752,17 +752,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
   }
 }
 
-// Pooled gradients: workgroup per (b, g, 64 pooled rows), four waves.
+// Pooled gradients: workgroup per (b, g, 64 pooled rows, chunk), four
+// waves.  The chunk's (query head, query block) pairs are taken 256 at a
+// time: each thread tests one pair against the selection bitmap (is any of
+// the 64 pooled rows in that query block's tail?) and the pairs that pass
+// are compacted in ascending order into LDS with the 64-bit mask of rows in
+// the tail.  Their query tiles then stream through double-buffered LDS like
+// the dk/dv pass: the next tile loads while the current one is used.
 template <int D, int BLK>
 __global__ __launch_bounds__(256, 2) void bwd_dtail_kernel(BwdArgs a) {
   constexpr int NW = 4;
   constexpr int SUB = BLK / BT;
+  constexpr int WIN = 64 * NW;                 // pairs tested per window
   using C = BC<D>;
   using DM = Dma<D, NW>;
-  __shared__ __attribute__((aligned(1024))) char Qt[C::TB];
-  __shared__ __attribute__((aligned(1024))) char Ot[C::TB];
-  __shared__ __attribute__((aligned(16))) float Lt[BT];
-  __shared__ __attribute__((aligned(16))) float Dt[BT];
+  __shared__ __attribute__((aligned(1024))) char Q0[C::TB];
+  __shared__ __attribute__((aligned(1024))) char Q1[C::TB];
+  __shared__ __attribute__((aligned(1024))) char O0[C::TB];
+  __shared__ __attribute__((aligned(1024))) char O1[C::TB];
+  __shared__ __attribute__((aligned(16))) float L0[BT];
+  __shared__ __attribute__((aligned(16))) float L1[BT];
+  __shared__ __attribute__((aligned(16))) float D0[BT];
+  __shared__ __attribute__((aligned(16))) float D1[BT];
+  __shared__ int xs[WIN];                      // passing pairs x = hl * M + I
+  __shared__ uint64_t xmask[WIN];              // their rows in the tail (bit j: row 64pt + j)
+  __shared__ int wcnt[NW];
 
   const int tiles = (a.M + BT - 1) / BT;
   const int chunk = blockIdx.x % kTailChunks;
@@ -792,30 +806,81 @@ __global__ __launch_bounds__(256, 2) void bwd_dtail_kernel(BwdArgs a) {
     acc.dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   // this workgroup's share of the (query head, query block) pairs x =
-  // hl * M + I; causal: only query blocks at or after these pooled rows
+  // hl * M + I
   const int GM = a.G * a.M;
   const int per = (GM + kTailChunks - 1) / kTailChunks;
   const int x1 = min(GM, (chunk + 1) * per);
-  for (int x = chunk * per; x < x1; ++x) {
-    const int hl = x / a.M, I = x - hl * a.M;
-    if (a.causal && I < BT * pt) continue;
-    const int bh = b * a.Hq + g * a.G + hl;
-    {
-      // pooled row Jl is in the tail of (bh, I): eligible and not listed
-      const uint32_t word = a.bits[((size_t)bh * a.M + I) * a.W + (j_ok ? Jl >> 5 : 0)];
-      const bool in = j_ok && (!a.causal || Jl <= I) && !((word >> (Jl & 31)) & 1u);
-      if (!__syncthreads_or(in)) continue;
-      const float lw = in ? lw_in : -INFINITY;
+  for (int xw = chunk * per; xw < x1; xw += WIN) {
+    // ---- test and compact: pooled row 64pt + j is in the tail of (bh, I)
+    // when it is eligible (below M, and at most I when causal) and not
+    // listed; words 2pt and 2pt + 1 of the bitmap row hold those 64 rows
+    uint64_t m = 0;
+    const int x = xw + t;
+    if (x < x1) {
+      const int hl = x / a.M, I = x - hl * a.M;
+      const int bh = b * a.Hq + g * a.G + hl;
+      const uint32_t* row = a.bits + ((size_t)bh * a.M + I) * a.W;
+      const uint32_t lo = row[2 * pt];
+      const uint32_t hi = 2 * pt + 1 < a.W ? row[2 * pt + 1] : 0xFFFFFFFFu;
+      const int lim = min(a.M, a.causal ? I + 1 : a.M) - BT * pt;
+      const uint64_t valid = lim >= 64 ? ~0ull : (lim <= 0 ? 0ull : (1ull << lim) - 1ull);
+      m = ~(((uint64_t)hi << 32) | lo) & valid;
+    }
+    const uint64_t bal = __ballot(m != 0);
+    if (lane == 0) wcnt[w] = __popcll(bal);
+    __syncthreads();
+    int base = 0, n = 0;
 #pragma unroll
-      for (int u = 0; u < SUB; ++u) {
-        const int q0 = I * a.block + BT * u;
-        if (q0 >= a.N) break;
-        issue_query_tile<D, NW>(a, bh, q0, Qt, Ot, Lt, Dt, w, voff);
-        wait_vm();
-        __syncthreads();
-        kv_tile<D, NW, true>(a, acc, Qt, Ot, Lt, Dt, fr, kf, vf, lg, lw, false, 0);
-        __syncthreads();
+    for (int i = 0; i < NW; ++i) {
+      base += i < w ? wcnt[i] : 0;
+      n += wcnt[i];
+    }
+    if (m != 0) {
+      const int pos = base + lanes_below(bal);
+      xs[pos] = x;
+      xmask[pos] = m;
+    }
+    __syncthreads();
+
+    // ---- the passing pairs' query tiles (SUB per query block), pipelined
+    const int n_t = n * SUB;
+    // tile tt: head row bh, first query row q0, this lane's log2 weight
+    auto tile_of = [&](int tt, int& bh, int& q0, float& lw) {
+      const int e = tt / SUB;
+      const int xe = xs[e];
+      const int hl = xe / a.M, I = xe - hl * a.M;
+      bh = b * a.Hq + g * a.G + hl;
+      q0 = I * a.block + BT * (tt % SUB);
+      lw = ((xmask[e] >> (16 * w + lr)) & 1ull) ? lw_in : -INFINITY;
+    };
+    int bh0 = 0, q00 = 0;
+    float lw0 = 0.f;
+    if (n_t > 0) {
+      tile_of(0, bh0, q00, lw0);
+      issue_query_tile<D, NW>(a, bh0, q00, Q0, O0, L0, D0, w, voff);
+    }
+    wait_vm();
+    __syncthreads();
+    auto step = [&](int tt, const char* Qc, const char* Oc, const float* Lc, const float* Dc, char* Qn, char* On,
+                    float* Ln, float* Dn) __attribute__((always_inline)) {
+      int bh1 = 0, q01 = 0;
+      float lw1 = 0.f;
+      if (tt + 1 < n_t) {
+        tile_of(tt + 1, bh1, q01, lw1);
+        issue_query_tile<D, NW>(a, bh1, q01, Qn, On, Ln, Dn, w, voff);
       }
+      // a sub-tile past the end of the sequence (the last block's second
+      // half) has no rows: skipped
+      if (q00 < a.N) kv_tile<D, NW, true>(a, acc, Qc, Oc, Lc, Dc, fr, kf, vf, lg, lw0, false, 0);
+      wait_vm();
+      __syncthreads();
+      bh0 = bh1;
+      q00 = q01;
+      lw0 = lw1;
+    };
+    for (int tt = 0; tt < n_t; tt += 2) {
+      step(tt, Q0, O0, L0, D0, Q1, O1, L1, D1);
+      if (tt + 1 < n_t) step(tt + 1, Q1, O1, L1, D1, Q0, O0, L0, D0);
     }
   }
   if (j_ok) {   // this chunk's partial sums
