@@ -111,3 +111,35 @@ def test_full_size_gradients(name):
             err, top = np.abs(got - ref).max(), np.abs(ref).max()
             say(f"  {nm} of head {g}: max-abs err {err:.3e}, max |ref| {top:.3e}")
             assert err <= REL * top, nm
+
+
+def test_pooled_pass_with_several_pair_windows():
+    """The pooled-gradient pass tests a range's (query head, query block)
+    pairs 256 at a time; with 16 query heads on one KV head and 300 blocks
+    each of its 16 ranges holds 300 pairs, so every range takes a second,
+    partial window.  Top-k at 15% leaves most of each row's weight in the
+    pooled tail, so pairs lost or doubled in either window would break the
+    dv identity by far more than its tolerance; dq of sampled blocks (no
+    pooled pass involved) is checked against the oracle as well."""
+    wl = get_config("dit_image_8k").replace(name="pooled_windows", Hq=16, Hkv=1, N=19200, d=64)
+    assert wl.approx and (wl.Hq // wl.Hkv) * wl.M > 256 * 16
+    say("pooled windows case: 16 query heads on one KV head, N = 19200, d = 64, top-k 15% + tail")
+    q, k, v = make_inputs(wl, seed=5)
+    dout = output_gradient(wl, seed=5)
+    mask, dq, dk, dv = _run(wl, q, k, v, dout)
+    ref = dout[0].sum(axis=(0, 1), dtype=np.float64)
+    got = dv[0, 0].sum(axis=0, dtype=np.float64)
+    mag = np.abs(dv[0, 0]).sum(axis=0, dtype=np.float64)
+    assert np.all(np.abs(got - ref) <= ID_REL * mag + 1e-3), "dv sum"
+    got = dk[0, 0].sum(axis=0, dtype=np.float64)
+    mag = np.abs(dk[0, 0]).sum(axis=0, dtype=np.float64)
+    assert np.all(np.abs(got) <= ID_REL * mag + 1e-3), "dk sum"
+    say("  identities hold")
+    scale = 1.0 / np.sqrt(wl.d)
+    elig = oracle.eligible_mask(wl.M, wl.causal)
+    for h, I in ((0, 0), (7, 150), (15, wl.M - 1)):
+        gq, _, _ = _block_grad(wl, q, k, v, dout, mask, 0, h, I, elig, scale)
+        r0 = I * wl.block
+        err, top = np.abs(dq[0, h, r0:r0 + gq.shape[0]] - gq).max(), np.abs(gq).max()
+        say(f"  dq (h={h}, I={I}): max-abs err {err:.3e}, max |ref| {top:.3e}")
+        assert err <= REL * top, (h, I)
