@@ -26,7 +26,7 @@ from ._lib import SA_DTYPE_BF16, SA_DTYPE_F32, SA_SELECT_ALPHA, SA_SELECT_DENSIT
 __all__ = [
     "Workspace", "block_pool", "block_sparse_attention", "buffer_sizes", "fwd", "make_desc",
     "route", "select", "SparseAttnError", "abi_version", "fwd_lse", "bwd_buffer_sizes",
-    "BwdWorkspace", "bwd",
+    "BwdWorkspace", "bwd", "check_lists",
 ]
 
 
@@ -119,9 +119,34 @@ def route(desc, q, k, v, q_bar, k_bar, v_sum, tail, blk_idx, blk_cnt, stream=Non
     _lib.check(st, "sparse_attn_route")
 
 
-def fwd(desc, q, k, v, k_bar, v_sum, tail, blk_idx, blk_cnt, out, stream=None) -> None:
+def check_lists(desc, blk_idx, blk_cnt, stream=None) -> dict:
+    """Validate block lists on the device (``sparse_attn_check_lists``) and
+    wait for the result: ``{"ok", "flags" (names of the violations), "bad_rows",
+    "first_bad_row"}``."""
+    import torch
+    res = torch.empty(4, dtype=torch.int32, device=blk_idx.device)
+    st = _lib.lib().sparse_attn_check_lists(desc, _ptr(blk_idx), _ptr(blk_cnt), _ptr(res), _stream(stream))
+    _lib.check(st, "sparse_attn_check_lists")
+    if stream is None:
+        torch.cuda.current_stream(blk_idx.device).synchronize()
+    else:
+        stream.synchronize()
+    flags, bad, first = (int(x) & 0xFFFFFFFF for x in res[:3].cpu().tolist())
+    return {"ok": flags == 0, "flags": [n for b, n in _lib.LIST_FLAGS.items() if flags & b],
+            "bad_rows": bad, "first_bad_row": None if bad == 0 else first}
+
+
+def fwd(desc, q, k, v, k_bar, v_sum, tail, blk_idx, blk_cnt, out, stream=None, check=False) -> None:
     """Stage 3: attention over the listed blocks (+ 0th-order tail when
-    approx: k_bar/v_sum for float32 inputs, tail for bf16 inputs)."""
+    approx: k_bar/v_sum for float32 inputs, tail for bf16 inputs).  With
+    ``check`` the lists are validated on the device first (``check_lists``,
+    which waits for the stream) and a bad list raises ValueError before the
+    attention is launched."""
+    if check:
+        r = check_lists(desc, blk_idx, blk_cnt, stream)
+        if not r["ok"]:
+            raise ValueError(f"invalid block lists: {r['flags']} in {r['bad_rows']} rows "
+                             f"(first row {r['first_bad_row']})")
     st = _lib.lib().sparse_attn_fwd(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(k_bar), _ptr(v_sum),
                                     _ptr(tail), _ptr(blk_idx), _ptr(blk_cnt), _ptr(out),
                                     _stream(stream))
@@ -203,17 +228,21 @@ def block_sparse_attention(q, k, v, *, block_size: int = 64, alpha: Optional[flo
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
     dt = "bf16" if q.dtype == torch.bfloat16 else "f32"
+    if workspace is not None and alpha is None and density is None:
+        # the selection rule is the one the workspace was built for
+        wd = workspace.desc
+        alpha, density = (wd.alpha, None) if wd.select_mode == SA_SELECT_ALPHA else (None, wd.density)
+    desc = make_desc(B, Hq, Hkv, N, d, block=block_size, dtype=dt, alpha=alpha, density=density,
+                     causal=causal, approx=approx, scale=scale)
     if workspace is None:
-        desc = make_desc(B, Hq, Hkv, N, d, block=block_size, dtype=dt, alpha=alpha, density=density,
-                         causal=causal, approx=approx, scale=scale)
         buffer_sizes(desc)   # validates before any allocation
         workspace = Workspace(desc, device=q.device)
     ws = workspace
-    desc = ws.desc
-    want_dt = SA_DTYPE_BF16 if q.dtype == torch.bfloat16 else SA_DTYPE_F32
-    if (tuple(q.shape) != (desc.batch, desc.heads_q, desc.seq_len, desc.head_dim)
-            or k.shape[1] != desc.heads_kv or desc.dtype != want_dt or ws.q_bar.device != q.device):
-        raise ValueError("workspace was built for another shape, dtype or device")
+    if ws.q_bar.device != q.device:
+        raise ValueError("workspace is on another device")
+    bad = [name for name, _ in SaDesc._fields_ if getattr(ws.desc, name) != getattr(desc, name)]
+    if bad:
+        raise ValueError(f"workspace was built for another problem (differs in {', '.join(bad)})")
     if out is None:
         out = torch.empty_like(q)
     elif (out.shape != q.shape or out.dtype != q.dtype or out.device != q.device

@@ -51,6 +51,9 @@ class SaBwdSizes(ctypes.Structure):
                                                "dv_bar")]
 
 
+LIST_FLAGS = {1: "count", 2: "range", 4: "order", 8: "ineligible", 16: "no_diagonal"}
+
+
 class SparseAttnError(ValueError):
     def __init__(self, status: int, what: str, text: str):
         super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({text})")
@@ -70,6 +73,7 @@ _SIGS = {
     "sparse_attn_fwd_lse": [ctypes.POINTER(SaDesc)] + [_P] * 11,
     "sparse_attn_bwd_buffer_sizes": [ctypes.POINTER(SaDesc), ctypes.POINTER(SaBwdSizes)],
     "sparse_attn_bwd": [ctypes.POINTER(SaDesc)] + [_P] * 19,
+    "sparse_attn_check_lists": [ctypes.POINTER(SaDesc), _P, _P, _P, _P],
     "sparse_attn_fwd": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "sparse_attn_status_string": [ctypes.c_int],
     "sparse_attn_abi_version": [],

@@ -185,6 +185,17 @@ SA_EXPORT sa_status sparse_attn_fwd(const sa_desc* desc, const void* q, const vo
   return fwd_impl(desc, q, k, v, k_bar, v_sum, tail, blk_idx, blk_cnt, out, nullptr, stream);
 }
 
+SA_EXPORT sa_status sparse_attn_check_lists(const sa_desc* desc, const int32_t* blk_idx,
+                                            const int32_t* blk_cnt, uint32_t* result, void* stream) {
+  sa::Shape s;
+  const sa_status st = check_desc(desc, &s);
+  if (st != SA_OK) return st;
+  if (!blk_idx || !blk_cnt || !result) return SA_ERR_NULL;
+  if (!aligned16(blk_idx) || !aligned16(blk_cnt) || !aligned16(result)) return SA_ERR_ALIGN;
+  return from_hip(sa::launch_check_lists(s, desc->causal, desc->approx, blk_idx, blk_cnt, result,
+                                         (hipStream_t)stream));
+}
+
 SA_EXPORT sa_status sparse_attn_bwd_buffer_sizes(const sa_desc* desc, sa_bwd_sizes* sizes) {
   sa::Shape s;
   const sa_status st = check_desc(desc, &s);

@@ -46,6 +46,11 @@ hipError_t launch_fwd(const Shape& s, const FwdParams& p, const void* q, const v
                       const void* v, const float* k_bar, const float* v_sum, const void* tail,
                       const int32_t* blk_idx, const int32_t* blk_cnt, void* out, hipStream_t st);
 
+// Validation of block lists: writes [flags, bad rows, first bad row] to
+// `result` (three device words; cleared by the launch itself).
+hipError_t launch_check_lists(const Shape& s, int causal, int approx, const int32_t* blk_idx,
+                              const int32_t* blk_cnt, uint32_t* result, hipStream_t st);
+
 // Gradients of stage 3 (bf16 inputs).
 struct BwdSizes {
   size_t lse, delta, sel_bits, col_idx, col_cnt, dk_bar, dv_bar;

@@ -74,8 +74,13 @@
  * Errors: argument errors return a non-zero sa_status before anything is
  * enqueued.  SA_ERR_HIP means a launch reported an error (hipGetLastError).
  * Faults inside a kernel surface at the caller's next synchronisation.
- * Caller-supplied block lists (sparse_attn_fwd) must satisfy the layout
- * above; they are not checked on the host.
+ * Caller-supplied block lists (sparse_attn_fwd, sparse_attn_fwd_lse,
+ * sparse_attn_bwd) must satisfy the layout above, and with causal=1 and
+ * approx=1 every row I must list its diagonal block I (the tail must not
+ * take the pooled key of the diagonal block, which holds later tokens).  The
+ * compute calls do not check lists (an entry outside [0, M) makes the
+ * kernels read and write out of bounds); sparse_attn_check_lists checks
+ * them on the device.
  *
  * Supported: head_dim in {64, 128}; block in {64, 128}; M <= 2048;
  * dtype float32 or bfloat16; heads_q a multiple of heads_kv.
@@ -90,7 +95,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 4
+#define SPARSE_ATTN_ABI_VERSION 5
 
 typedef enum {
   SA_OK = 0,
@@ -169,6 +174,26 @@ sa_status sparse_attn_fwd(const sa_desc* desc, const void* q, const void* k, con
                           const float* k_bar, const float* v_sum, const void* tail,
                           const int32_t* blk_idx, const int32_t* blk_cnt, void* out,
                           void* stream);
+
+/* Violation flags of sparse_attn_check_lists (OR-ed over all rows). */
+enum {
+  SA_LIST_COUNT = 1,        /* blk_cnt outside [1, |E_I|] (|E_I| = M, or I + 1 if causal) */
+  SA_LIST_RANGE = 2,        /* an entry outside [0, M)                                   */
+  SA_LIST_ORDER = 4,        /* entries not strictly ascending                            */
+  SA_LIST_INELIGIBLE = 8,   /* causal: an entry J > I                                     */
+  SA_LIST_NO_DIAGONAL = 16  /* causal with approx: the row does not list its block I      */
+};
+
+/* Check caller-built block lists on the device, one wave per row, against
+ * the layout the attention kernels rely on (the lists of sparse_attn_select
+ * always pass).  Writes three uint32 to `result` (device memory, 16-byte
+ * aligned): the OR of the SA_LIST_* flags of every bad row (0 = all rows
+ * valid), the number of bad rows, and the lowest bad row index
+ * ((b * heads_q + h) * M + I; 0xFFFFFFFF if none).  Reads at most M entries
+ * per row.  Asynchronous like the other calls: read `result` after the
+ * stream has completed.  Errors: as sparse_attn_fwd's argument checks. */
+sa_status sparse_attn_check_lists(const sa_desc* desc, const int32_t* blk_idx, const int32_t* blk_cnt,
+                                  uint32_t* result, void* stream);
 
 /* ---- Training: gradients of stage 3 (PISA explainer, "minimal documented
  * usage": the simplified 0th-order variant is the one that supports

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
     h = _lib.lib()
     for name in _declared():
         assert hasattr(h, name), name
-    assert bsa.abi_version() == 4
+    assert bsa.abi_version() == 5
 
 
 @pytest.mark.skipif(not os.path.exists(_lib.PEAKS_PATH), reason="libsa_peaks.so not built")
@@ -194,3 +194,4 @@ def test_one_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     runtimes = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(runtimes) == 1, runtimes
+

@@ -215,8 +215,19 @@ def test_wrapper_rejects_mismatched_workspace_and_out():
         bsa.block_sparse_attention(qd, kd, vd, density=0.2,
                                    out=torch.empty((1, 2, 256, 32), dtype=torch.bfloat16, device="cuda"))
     ws = bsa.Workspace(bsa.make_desc(1, 2, 2, 256, 64, block=64, dtype="bf16", density=0.2))
+    # a workspace carries its descriptor: any argument that contradicts it
+    # (rule, threshold, block, causal, tail, scale) is refused, not ignored
+    for kw in (dict(density=0.3), dict(alpha=0.5), dict(density=0.2, causal=True),
+               dict(density=0.2, approx=False), dict(density=0.2, block_size=128),
+               dict(density=0.2, scale=0.5)):
+        with pytest.raises(ValueError, match="another problem"):
+            bsa.block_sparse_attention(qd, kd, vd, workspace=ws, **kw)
     out = torch.empty_like(qd)
     o = bsa.block_sparse_attention(qd, kd, vd, density=0.2, workspace=ws, out=out)
+    # without a rule argument the workspace's rule is used
+    o2 = bsa.block_sparse_attention(qd, kd, vd, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
     torch.cuda.synchronize()
     assert o.data_ptr() == out.data_ptr()
     gpu_mask = lists_to_mask(to_host(ws.blk_idx), to_host(ws.blk_cnt))
