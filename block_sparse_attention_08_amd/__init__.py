@@ -26,7 +26,7 @@ from ._lib import SA_DTYPE_BF16, SA_DTYPE_F32, SA_SELECT_ALPHA, SA_SELECT_DENSIT
 __all__ = [
     "Workspace", "block_pool", "block_sparse_attention", "buffer_sizes", "fwd", "make_desc",
     "route", "select", "SparseAttnError", "abi_version", "fwd_lse", "bwd_buffer_sizes",
-    "BwdWorkspace", "bwd", "check_lists",
+    "BwdWorkspace", "bwd", "bwd_noalloc", "bwd_noalloc_scratch", "check_lists",
 ]
 
 
@@ -199,6 +199,26 @@ def bwd(desc, q, k, v, tail, blk_idx, blk_cnt, out, dout, bws: BwdWorkspace, dq,
                                     _ptr(bws.dk_bar), _ptr(bws.dv_bar), _ptr(dq), _ptr(dk), _ptr(dv),
                                     _stream(stream))
     _lib.check(st, "sparse_attn_bwd")
+
+
+def bwd_noalloc_scratch(desc: SaDesc) -> tuple:
+    """(bytes of scratch ``bwd_noalloc`` needs for ``desc``, bytes the
+    library's fixed scratch array holds); host-only call."""
+    import ctypes
+    need, cap = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _lib.check(_lib.lib().sparse_attn_bwd_noalloc_scratch(desc, ctypes.byref(need), ctypes.byref(cap)),
+               "sparse_attn_bwd_noalloc_scratch")
+    return int(need.value), int(cap.value)
+
+
+def bwd_noalloc(desc, q, k, v, tail, blk_idx, blk_cnt, out, lse, dout, dq, dk, dv, stream=None) -> None:
+    """``bwd`` without caller scratch: the library's fixed per-device scratch
+    array stands in for the ``BwdWorkspace`` buffers (for callers that cannot
+    allocate).  Calls that overlap on one device race on that array."""
+    st = _lib.lib().sparse_attn_bwd_noalloc(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(tail), _ptr(blk_idx),
+                                            _ptr(blk_cnt), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                            _ptr(dk), _ptr(dv), _stream(stream))
+    _lib.check(st, "sparse_attn_bwd_noalloc")
 
 
 def _check_tensors(q, k, v):

@@ -20,7 +20,7 @@ SA_SELECT_ALPHA, SA_SELECT_DENSITY = 0, 1
 
 STATUS_NAMES = {
     0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_DTYPE", 4: "SA_ERR_PARAM",
-    5: "SA_ERR_ALIGN", 6: "SA_ERR_UNSUPPORTED", 7: "SA_ERR_HIP",
+    5: "SA_ERR_ALIGN", 6: "SA_ERR_UNSUPPORTED", 7: "SA_ERR_HIP", 8: "SA_ERR_SCRATCH",
 }
 
 
@@ -73,7 +73,10 @@ _SIGS = {
     "sparse_attn_fwd_lse": [ctypes.POINTER(SaDesc)] + [_P] * 11,
     "sparse_attn_bwd_buffer_sizes": [ctypes.POINTER(SaDesc), ctypes.POINTER(SaBwdSizes)],
     "sparse_attn_bwd": [ctypes.POINTER(SaDesc)] + [_P] * 19,
+    "sparse_attn_bwd_noalloc": [ctypes.POINTER(SaDesc)] + [_P] * 13,
     "sparse_attn_check_lists": [ctypes.POINTER(SaDesc), _P, _P, _P, _P],
+    "sparse_attn_bwd_noalloc_scratch": [ctypes.POINTER(SaDesc), ctypes.POINTER(ctypes.c_size_t),
+                                        ctypes.POINTER(ctypes.c_size_t)],
     "sparse_attn_fwd": [ctypes.POINTER(SaDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "sparse_attn_status_string": [ctypes.c_int],
     "sparse_attn_abi_version": [],

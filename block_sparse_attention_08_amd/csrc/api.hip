@@ -78,6 +78,7 @@ SA_EXPORT const char* sparse_attn_status_string(sa_status st) {
     case SA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case SA_ERR_UNSUPPORTED: return "unsupported head_dim, block or number of blocks";
     case SA_ERR_HIP: return "the HIP runtime reported an error";
+    case SA_ERR_SCRATCH: return "the problem needs more scratch than the library's fixed array holds";
   }
   return "unknown status";
 }

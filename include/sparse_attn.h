@@ -95,7 +95,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 5
+#define SPARSE_ATTN_ABI_VERSION 6
 
 typedef enum {
   SA_OK = 0,
@@ -105,7 +105,9 @@ typedef enum {
   SA_ERR_PARAM = 4,        /* alpha / density / select_mode / flags out of range   */
   SA_ERR_ALIGN = 5,        /* a tensor pointer is not 16-byte aligned              */
   SA_ERR_UNSUPPORTED = 6,  /* valid in principle, not built (head_dim, block, M)   */
-  SA_ERR_HIP = 7           /* the HIP runtime reported an error at launch          */
+  SA_ERR_HIP = 7,          /* the HIP runtime reported an error at launch          */
+  SA_ERR_SCRATCH = 8       /* the problem needs more than the library's fixed
+                              scratch (sparse_attn_bwd_noalloc only)              */
 } sa_status;
 
 enum { SA_DTYPE_F32 = 0, SA_DTYPE_BF16 = 1 };
@@ -236,6 +238,30 @@ sa_status sparse_attn_bwd(const sa_desc* desc, const void* q, const void* k, con
                           const void* out, const float* lse, const void* dout, float* delta,
                           uint32_t* sel_bits, int32_t* col_idx, int32_t* col_cnt, float* dk_bar,
                           float* dv_bar, void* dq, void* dk, void* dv, void* stream);
+
+/* ---- For callers that cannot allocate (code under HIP graph capture,
+ * serving loops or harnesses that forbid hipMalloc): sparse_attn_bwd with
+ * its scratch taken from a fixed array of device memory that the library
+ * owns, instead of caller buffers.  The array holds
+ * SPARSE_ATTN_BWD_NOALLOC_SCRATCH_BYTES on each device the entry point runs
+ * on, from its first call there until the process ends; the entry point
+ * itself calls no allocator.  It runs the same kernels as sparse_attn_bwd and
+ * gives the same results.  All calls on one device share its array: calls on
+ * one stream are ordered, calls that overlap on one device (several streams
+ * or threads) race and must not be made.  `stream` must belong to the
+ * current device.  The scratch need is the sum of sparse_attn_bwd_buffer_sizes'
+ * delta, sel_bits, col_idx, col_cnt, dk_bar and dv_bar, each rounded up to
+ * 256 bytes; beyond the array the call returns SA_ERR_SCRATCH before any
+ * launch.  Other errors as for sparse_attn_bwd. */
+#define SPARSE_ATTN_BWD_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* Scratch bytes `desc` needs (*need) and the array's size (*cap); host only. */
+sa_status sparse_attn_bwd_noalloc_scratch(const sa_desc* desc, size_t* need, size_t* cap);
+
+sa_status sparse_attn_bwd_noalloc(const sa_desc* desc, const void* q, const void* k, const void* v,
+                                  const void* tail, const int32_t* blk_idx, const int32_t* blk_cnt,
+                                  const void* out, const float* lse, const void* dout, void* dq,
+                                  void* dk, void* dv, void* stream);
 
 /* Static, human-readable text of a status code. */
 const char* sparse_attn_status_string(sa_status status);

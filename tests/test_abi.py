@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
     h = _lib.lib()
     for name in _declared():
         assert hasattr(h, name), name
-    assert bsa.abi_version() == 5
+    assert bsa.abi_version() == 6
 
 
 @pytest.mark.skipif(not os.path.exists(_lib.PEAKS_PATH), reason="libsa_peaks.so not built")
@@ -65,7 +65,7 @@ def test_peaks_library_exports_and_rejects_bad_arguments():
 @needs_lib
 def test_status_strings():
     h = _lib.lib()
-    for code in range(8):
+    for code in range(9):
         s = h.sparse_attn_status_string(code).decode()
         assert s and s != "unknown status"
     assert h.sparse_attn_status_string(99).decode() == "unknown status"
@@ -195,3 +195,24 @@ def test_one_hip_runtime_in_process():
     runtimes = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(runtimes) == 1, runtimes
 
+
+@needs_lib
+def test_noalloc_backward_scratch_limit():
+    """The allocation-free backward takes its scratch from a fixed array:
+    the need is the backward's scratch buffers (lse excluded, which the
+    caller holds), each rounded up to 256 bytes; a problem beyond the array
+    is refused with SA_ERR_SCRATCH before any device call."""
+    d = _desc()                      # 8K image layer: fits
+    need, cap = bsa.bwd_noalloc_scratch(d)
+    s = bsa.bwd_buffer_sizes(d)
+    up = lambda x: -(-x // 256) * 256   # noqa: E731
+    assert need == sum(up(s[n]) for n in ("delta", "sel_bits", "col_idx", "col_cnt", "dk_bar", "dv_bar"))
+    assert cap == 64 << 20 and need <= cap
+    big = _desc(N=131072, block=128, Hq=32, Hkv=8, density=None, alpha=0.5, causal=True)
+    need_big, _ = bsa.bwd_noalloc_scratch(big)
+    assert need_big > cap
+    h = _lib.lib()
+    bad = ctypes.c_void_p(0x1000)
+    assert h.sparse_attn_bwd_noalloc(big, *([bad] * 12), None) == 8
+    assert h.sparse_attn_bwd_noalloc(_desc(dtype="f32", d=64), *([bad] * 12), None) == 6
+    assert h.sparse_attn_bwd_noalloc_scratch(d, None, None) == 1

@@ -1,0 +1,72 @@
+"""sparse_attn_bwd_noalloc (scratch from the library's fixed device array)
+against sparse_attn_bwd (scratch from caller buffers), through the C ABI:
+the same kernels on the same inputs, so the gradients must agree bit for
+bit.  Two calls in a row on one device, the second on a smaller problem, so
+the second runs over the first one's leftovers in the shared array."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import say, to_dev
+from synth import random_qkv
+
+pytestmark = pytest.mark.gpu
+
+# (B, Hq, Hkv, N, d, block, causal, approx, mode): the larger problem first
+CALLS = [
+    (1, 4, 2, 2600, 128, 128, True, True, "alpha"),    # causal + tail, GQA, ragged
+    (1, 2, 1, 700, 64, 64, False, True, "density"),    # smaller: d = 64, 64-row blocks
+]
+
+
+def _grads(case, seed):
+    import torch
+    import block_sparse_attention_08_amd as bsa
+    B, Hq, Hkv, N, d, block, causal, approx, mode = case
+    q, k, v = random_qkv(B, Hq, Hkv, N, d, seed=seed, block=block, dtype="bf16", kind="cluster", noise=0.5)
+    dout = random_qkv(B, Hq, Hq, N, d, seed=seed + 1, block=block, dtype="bf16")[0]
+    desc = bsa.make_desc(B, Hq, Hkv, N, d, block=block, dtype="bf16",
+                         alpha=0.5 if mode == "alpha" else None,
+                         density=0.2 if mode == "density" else None, causal=causal, approx=approx)
+    need, cap = bsa.bwd_noalloc_scratch(desc)
+    assert need <= cap
+    qd, kd, vd, gd = (to_dev(x, "bf16") for x in (q, k, v, dout))
+    ws = bsa.Workspace(desc)
+    bws = bsa.BwdWorkspace(desc)
+    bsa.block_pool(desc, qd, kd, vd, ws.q_bar, ws.k_bar, ws.v_sum, ws.tail)
+    bsa.select(desc, ws.q_bar, ws.k_bar, ws.blk_idx, ws.blk_cnt)
+    out = torch.empty_like(qd)
+    bsa.fwd_lse(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, ws.blk_idx, ws.blk_cnt, out, bws.lse)
+    # the allocation-free entry point first (in a fresh process: its first
+    # call on the device), then the one with caller scratch
+    na = [torch.full_like(qd, float("nan")), torch.full_like(kd, float("nan")), torch.full_like(vd, float("nan"))]
+    bsa.bwd_noalloc(desc, qd, kd, vd, ws.tail, ws.blk_idx, ws.blk_cnt, out, bws.lse, gd, *na)
+    wa = [torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)]
+    bsa.bwd(desc, qd, kd, vd, ws.tail, ws.blk_idx, ws.blk_cnt, out, gd, bws, *wa)
+    torch.cuda.synchronize()
+    return na, wa, ws, (q, k, v, dout)
+
+
+def test_noalloc_backward_matches_workspace_backward():
+    import torch
+    for i, case in enumerate(CALLS):
+        say("noalloc call", i, case)
+        na, wa, ws, host = _grads(case, seed=41 + 2 * i)
+        for name, a, b in zip(("dq", "dk", "dv"), na, wa):
+            assert torch.isfinite(a.float()).all(), name
+            assert torch.equal(a, b), f"{name} differs from sparse_attn_bwd"
+        # and the gradients are the method's (oracle at its bound, one tensor)
+        B, Hq, Hkv, N, d, block, causal, approx, mode = case
+        q, k, v, dout = host
+        cnt = ws.blk_cnt.cpu().numpy()
+        idx = ws.blk_idx.cpu().numpy()
+        M = cnt.shape[-1]
+        sel = np.zeros(cnt.shape + (M,), bool)
+        for pos in np.ndindex(*cnt.shape):
+            sel[pos + (idx[pos][:cnt[pos]],)] = True
+        gr = oracle.backward(q, k, v, dout, sel, block=block, causal=causal, approx=approx)
+        dq = na[0].float().cpu().numpy()
+        err = np.abs(dq - gr["dq"]).max()
+        say(f"  dq vs oracle: max-abs {err:.3e} of max |ref| {np.abs(gr['dq']).max():.3e}")
+        assert err <= 2e-2 * np.abs(gr["dq"]).max()
