@@ -4,8 +4,15 @@
 
 One step = one layer: block pooling, scoring + selection, and attention over
 all heads of the workload, with inputs already resident in HBM.  Default
-workload: dit_image_8k (bf16, B=1, 24 heads, N=8192, d=128, block 64, top-k
-at density 0.15, 0th-order tail).  Prints one JSON line.
+workload: llm_prefill_256k (bf16, B=1, 8 heads, N=262144, d=128, block 128,
+causal, alpha=0.5 threshold, no tail), the top of the 8K-256K range the
+metric is quoted over.  Prints one JSON line.
+
+Beside the timed steps: the dense comparison (the same attention kernel with
+every eligible block listed, timed on its own launches; its speed-up and its
+output difference from the sparse run), and the oracle on whole KV groups,
+timed step by step on the host cores and checked against the timed run's
+lists and outputs.
 
 Stage times come from HIP events recorded on the stream the library launches
 on (torch's current stream) around every stage of every timed step.  The
@@ -49,17 +56,21 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="dit_image_8k")
+    p.add_argument("--workload", default="llm_prefill_256k")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-peaks", action="store_true",
                    help="skip the achievable-rate kernels (streaming read, MFMA loop)")
     p.add_argument("--cpu-budget-s", type=float, default=12.0,
-                   help="CPU seconds the oracle sample may take (whole heads)")
+                   help="CPU seconds the oracle sample may take (whole KV groups, at least one)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run one device copy of this size (counter calibration runs)")
     p.add_argument("--dense", action="store_true",
-                   help="attend every eligible block (caller lists), the dense comparison run")
+                   help="attend every eligible block (caller lists) in the timed steps")
+    p.add_argument("--no-dense-compare", action="store_true",
+                   help="skip the in-run dense comparison (every eligible block listed, same kernel)")
+    p.add_argument("--dense-steps", type=int, default=3,
+                   help="timed launches of the dense comparison")
     p.add_argument("--backward", action="store_true",
                    help="also run the gradients (fwd_lse + bwd) each step and report them")
     p.add_argument("--no-graph", action="store_true",
@@ -188,49 +199,168 @@ def achievable_peaks(dev, read_mib=2048, reps=5, mfma_iters=20000, lds_iters=200
     return got.value / t_read / 1e9, flops.value / t_mfma / 1e12, lds.value / t_lds / 1e9 / cus
 
 
-def cpu_baseline(wl, seed, budget_s):
-    """Time the oracle (as it stands) on whole KV groups of the workload until
-    about `budget_s` of oracle time is spent, in KV-group order; when the whole
-    workload takes less, further passes over it repeat the measurement.
-    Returns effective TFLOP/s with the same work count as the GPU figure."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, seed, budget_s, gpu=None):
+    """Time the oracle (as it stands, float64 numpy) on whole KV groups of
+    the workload, in KV-group order, until about `budget_s` of oracle time is
+    spent (at least one group; further passes when the workload takes less).
+    Each step of the method is timed on its own: pooling, block scores,
+    selection (mask and thresholds), attention of every query block.
+
+    With `gpu` = (blk_idx, blk_cnt, out) device tensors of the timed GPU run,
+    the first pass over each group is also a parity check of that run: the
+    GPU's lists against the oracle's (bit-exact outside the 1e-5 band around
+    the threshold; band blocks counted) and the GPU's outputs against the
+    oracle's on every query block whose selection agrees (max-abs)."""
     import oracle
     from synth import make_group
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = 1
+        blas_threads = None
     G = wl.Hq // wl.Hkv
-    spent = 0.0
+    M = wl.M
+    scale = 1.0 / np.sqrt(wl.d)
+    bounds = oracle.block_bounds(wl.N, wl.block)
+    elig = oracle.eligible_mask(M, wl.causal)
+    t_stage = {"pool_s": 0.0, "score_s": 0.0, "select_s": 0.0, "attend_s": 0.0}
     flops = 0.0
     groups = 0
-    cache = {}
-    while spent < budget_s or groups == 0:
+    par = {"heads": 0, "band_blocks": 0, "band_differ": 0, "mismatch_out_of_band": 0,
+           "blocks_compared": 0, "blocks_skipped": 0, "max_abs_err": 0.0}
+    checked = set()
+    while sum(t_stage.values()) < budget_s or groups == 0:
         g = groups % wl.Hkv
-        if g not in cache:
-            q, k, v = make_group(wl, seed, 0, g)
-            cache[g] = (q, k, v) if wl.N * wl.d * (G + 2) * 4 <= (1 << 28) else None
-        q, k, v = cache[g] if cache[g] is not None else make_group(wl, seed, 0, g)
+        q, k, v = make_group(wl, seed, 0, g)
+        qb4, kb4 = q[None], k[None, None]
         t0 = time.perf_counter()
-        r = oracle.forward(q[None], k[None, None], v[None, None], block=wl.block,
-                           causal=wl.causal, approx=wl.approx, mode=wl.select, alpha=wl.alpha,
-                           density=wl.density)
-        spent += time.perf_counter() - t0
-        idx, cnt = oracle.mask_to_lists(r["mask"])
+        q_bar = oracle.pool_mean(qb4, wl.block)
+        k_bar = oracle.pool_mean(kb4, wl.block)
+        v_sum = oracle.pool_sum(v[None, None], wl.block) if wl.approx else None
+        t1 = time.perf_counter()
+        sc = oracle.block_scores(q_bar, k_bar, scale)
+        t2 = time.perf_counter()
+        sel = oracle.select(sc, causal=wl.causal, approx=wl.approx, mode=wl.select, alpha=wl.alpha,
+                            density=wl.density)
+        thr = oracle.thresholds(sc, causal=wl.causal, mode=wl.select, alpha=wl.alpha, density=wl.density)
+        t3 = time.perf_counter()
+        out = np.empty((G, wl.N, wl.d))
+        for hl in range(G):
+            for I in range(M):
+                r0, r1 = bounds[I]
+                out[hl, r0:r1] = oracle.attend_block(
+                    q[hl, r0:r1], r0, k, v, k_bar[0, 0], None if v_sum is None else v_sum[0, 0],
+                    sel[0, hl, I], elig[I], block=wl.block, scale=scale, causal=wl.causal, approx=wl.approx)
+        t4 = time.perf_counter()
+        t_stage["pool_s"] += t1 - t0
+        t_stage["score_s"] += t2 - t1
+        t_stage["select_s"] += t3 - t2
+        t_stage["attend_s"] += t4 - t3
+        idx, cnt = oracle.mask_to_lists(sel)
         ex, tl = work_units(idx, cnt, wl.N, wl.block, wl.causal, wl.approx)
         flops += 4.0 * wl.d * (ex + tl)
+        if gpu is not None and g not in checked:
+            checked.add(g)
+            gidx, gcnt, gout = gpu
+            heads = list(range(g * G, (g + 1) * G))
+            gc = gcnt[0, heads].cpu().numpy()
+            gi = gidx[0, heads].cpu().numpy()
+            gmask = np.zeros((1, G, M, M), bool)
+            for hl in range(G):
+                for I in range(M):
+                    gmask[0, hl, I, gi[hl, I, :gc[hl, I]]] = True
+            band = oracle.band_mask(sc, thr, wl.causal)
+            diff = gmask != sel
+            par["heads"] += G
+            par["band_blocks"] += int(band.sum())
+            par["band_differ"] += int((diff & band).sum())
+            par["mismatch_out_of_band"] += int((diff & ~band).sum())
+            rows_ok = ~diff.any(-1)[0]
+            go = gout[0, heads].float().cpu().numpy()
+            for hl in range(G):
+                for I in range(M):
+                    if not rows_ok[hl, I]:
+                        par["blocks_skipped"] += 1
+                        continue
+                    r0, r1 = bounds[I]
+                    e = float(np.abs(go[hl, r0:r1] - out[hl, r0:r1]).max())
+                    par["max_abs_err"] = max(par["max_abs_err"], e)
+                    par["blocks_compared"] += 1
         groups += 1
+    spent = sum(t_stage.values())
     if groups >= wl.Hkv:
         what = (f"all {wl.Hq} query heads, {groups / wl.Hkv:.2f} passes over the workload"
                 if groups % wl.Hkv else f"all {wl.Hq} query heads x {groups // wl.Hkv} passes")
     else:
         what = f"{groups * G} of {wl.Hq} query heads (KV groups 0..{groups - 1})"
-    return {
-        "value": flops / spent / 1e12, "unit": "TFLOP/s (effective)", "cores": int(threads),
-        "kind": "oracle",
-        "sample": f"{what}, full sequence, float64 numpy oracle: pool+score+select+attend, "
-                  f"{spent:.1f} s",
+    res = {
+        "value": flops / spent / 1e12, "unit": "TFLOP/s (effective)",
+        "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+        "sample": f"{what}, full sequence, every query block: float64 numpy oracle, "
+                  f"pool+score+select+attend, {spent:.1f} s",
+        "cpu_model": _cpu_model(), "blas_threads": blas_threads,
+        "stage_s": {k_: round(v_, 3) for k_, v_ in t_stage.items()},
+        "fraction_of_layer": round(groups / wl.Hkv, 4),
     }
+    if gpu is not None:
+        res["parity"] = par
+    return res
+
+
+def dense_compare(args, wl, desc, ws, qd, kd, vd, out, ms_step, ms_fwd, sparse_flops):
+    """The same attention kernel on caller lists holding every eligible
+    block (dense attention, causal if the workload is), timed with events on
+    the launch stream over its own launches after one warmup launch; the
+    routing stages are the sparse run's.  Returns its times, the speed-up of
+    the sparse layer and the difference between the two outputs."""
+    import torch
+    import block_sparse_attention_08_amd as bsa
+    M = wl.M
+    dev = qd.device
+    idx = torch.arange(M, dtype=torch.int32, device=dev).expand(wl.B, wl.Hq, M, M).contiguous()
+    if wl.causal:
+        cnt = torch.arange(1, M + 1, dtype=torch.int32, device=dev).expand(wl.B, wl.Hq, M).contiguous()
+    else:
+        cnt = torch.full((wl.B, wl.Hq, M), M, dtype=torch.int32, device=dev)
+    dout = torch.empty_like(out)
+    bsa.fwd(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, idx, cnt, dout)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.dense_steps):
+        bsa.fwd(desc, qd, kd, vd, ws.k_bar, ws.v_sum, ws.tail, idx, cnt, dout)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.dense_steps
+    ex, tl = work_units(idx.cpu().numpy(), cnt.cpu().numpy(), wl.N, wl.block, wl.causal, False)
+    dflops = 4.0 * wl.d * (ex + tl)
+    diff = (out.float() - dout.float()).abs()
+    ms_layer = ms_step - ms_fwd + ms
+    res = {
+        "fwd_ms": round(ms, 3), "layer_ms": round(ms_layer, 3),
+        "speedup_layer": round(ms_layer / ms_step, 2), "speedup_fwd": round(ms / ms_fwd, 2),
+        "algorithmic_gflop": round(dflops / 1e9, 1),
+        "TFLOPs": round(dflops / (ms * 1e-3) / 1e12, 1),
+        "frac_of_bf16_peak": round(dflops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "sparse_flop_share": round(sparse_flops / dflops, 5),
+        "max_abs_diff_sparse_vs_dense": round(float(diff.max()), 5),
+        "mean_abs_diff_sparse_vs_dense": round(float(diff.mean()), 6),
+        "launches": args.dense_steps,
+    }
+    del idx, cnt, dout, diff
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -450,9 +580,13 @@ def main():
             "fwd_frac_of_achievable_mfma": (round(eff_tflops_fwd / mfma, 4)
                                             if wl.dtype == "bf16" else None),
         }
+    if not (args.dense or args.no_dense_compare or args.backward):
+        print("[bench] dense comparison: every eligible block listed", file=sys.stderr, flush=True)
+        result["dense_compare"] = dense_compare(args, wl, desc, ws, qd, kd, vd, out, ms_step, ms_fwd, flops)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, args.seed, args.cpu_budget_s)
+        gpu = None if (args.dense or args.backward) else (ws.blk_idx, ws.blk_cnt, out)
+        result["cpu_baseline"] = cpu_baseline(wl, args.seed, args.cpu_budget_s, gpu=gpu)
     print(json.dumps(result), flush=True)
 
 
