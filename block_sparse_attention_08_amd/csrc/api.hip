@@ -28,8 +28,10 @@ sa_status check_desc(const sa_desc* d, sa::Shape* s) {
   if (isnan(d->scale) || isinf(d->scale)) return SA_ERR_PARAM;
   if (d->head_dim != 64 && d->head_dim != 128) return SA_ERR_UNSUPPORTED;
   if (d->block != 64 && d->block != 128) return SA_ERR_UNSUPPORTED;
-  const int M = (d->seq_len + d->block - 1) / d->block;
-  if (M > sa::kMaxBlocks) return SA_ERR_UNSUPPORTED;
+  // in 64 bits: seq_len + block - 1 overflows an int near INT32_MAX
+  const int64_t M64 = ((int64_t)d->seq_len + d->block - 1) / d->block;
+  if (M64 > sa::kMaxBlocks) return SA_ERR_UNSUPPORTED;
+  const int M = (int)M64;
   if ((int64_t)d->batch * d->heads_q > 65535) return SA_ERR_UNSUPPORTED;   // grid z of the score pass
   // every workgroup count and per-row index of the kernels is a 32-bit int
   const int64_t items = (int64_t)d->batch * (d->heads_q + 2 * (int64_t)d->heads_kv) * M;
