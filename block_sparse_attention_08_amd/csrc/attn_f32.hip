@@ -1,11 +1,12 @@
 // Stage 3 for float32 inputs: exact attention over the listed key blocks
 // plus the 0th-order tail, on the vector ALUs in float32.
 //
-// One workgroup (four waves) per 16 query rows of a (batch, head, query
+// One workgroup (eight waves) per 4 query rows of a (batch, head, query
 // block), sixteen lanes per query token (each owning D/16 of the head
 // dimension; the dot products are summed over the sixteen lanes with four
-// lane swaps).
-// Keys are visited in chunks of 64 staged in LDS; each chunk updates the
+// lane swaps).  Each wave holds all 4 rows and takes every eighth chunk of
+// the keys; the eight partial softmax states are merged at the end.
+// Keys are visited in chunks of 16 staged in LDS; each chunk updates the
 // running max m, sum l and output o of the online softmax (FlashAttention
 // tutorial, section 2: m <- max(m, max z); l <- l e^{m_old-m} + sum e^{z-m};
 // o <- o e^{m_old-m} + sum e^{z-m} v; answer o / l), evaluated in base 2
@@ -23,9 +24,10 @@ namespace sa {
 namespace {
 
 constexpr int kLanes = 16;              // lanes per query row, each owning D/16 dimensions
-constexpr int kRows = 16;               // query rows per workgroup (four waves)
-constexpr int kThreads = kLanes * kRows;
-constexpr int kChunk = 64;              // keys staged per LDS chunk
+constexpr int kRows = kWave / kLanes;   // query rows per workgroup (all of them in every wave)
+constexpr int kSplit = 8;               // waves per workgroup, each folding every 8th key chunk
+constexpr int kThreads = kWave * kSplit;
+constexpr int kChunk = 16;              // keys staged per LDS chunk
 constexpr int kSub = 16;                // keys per online-softmax update
 
 struct FwdArgs {
@@ -133,46 +135,57 @@ __device__ __forceinline__ void fold_chunk(State<D>& st, const float (*Ks)[D], c
   }
 }
 
-// One chunk of rows [0, n) of a [rows, D] float32 matrix moved through
-// registers: load() issues this thread's share of global loads (zeros past
-// row n), store() writes them to LDS.
+// One chunk of rows [0, n) of a [rows, D] float32 matrix moved through one
+// wave's registers: load() issues this lane's share of global loads (zeros
+// past row n), store() writes them to the wave's LDS chunk.
 template <int D>
 struct ChunkRegs {
-  static constexpr int NPF = kChunk * (D / 4) / kThreads;   // float4 per thread
-  static_assert(NPF * kThreads == kChunk * (D / 4), "chunk staging layout");
+  static constexpr int NPF = kChunk * (D / 4) / kWave;   // float4 per lane
+  static_assert(NPF * kWave == kChunk * (D / 4), "chunk staging layout");
   float4 x[NPF];
-  __device__ __forceinline__ void load(const float* src, int n) {
+  __device__ __forceinline__ void load(const float* src, int n, int lane) {
     const float4* s4 = reinterpret_cast<const float4*>(src);
 #pragma unroll
     for (int i = 0; i < NPF; ++i) {
-      const int u = threadIdx.x + i * kThreads;
+      const int u = lane + i * kWave;
       x[i] = u < n * (D / 4) ? s4[u] : float4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  __device__ __forceinline__ void store(float (*dst)[D]) const {
+  __device__ __forceinline__ void store(float (*dst)[D], int lane) const {
 #pragma unroll
-    for (int i = 0; i < NPF; ++i) reinterpret_cast<float4*>(dst[0])[threadIdx.x + i * kThreads] = x[i];
+    for (int i = 0; i < NPF; ++i) reinterpret_cast<float4*>(dst[0])[lane + i * kWave] = x[i];
   }
 };
 
+// Workgroup: kRows query rows, kSplit waves.  Every wave holds all kRows
+// rows (16 lanes each) and folds every kSplit-th chunk of the key sequence
+// into its own running (m, l, o); the kSplit partial states are merged at
+// the end (m = max_s m_s, l = sum_s l_s 2^{m_s - m}, o likewise: the online
+// softmax recurrence applied to whole partial sums).  Splitting the keys
+// over the waves, with no barrier inside the chunk loop, shortens each
+// workgroup's chain of dependent loads and folds, and the small row count
+// spreads a short sequence over many workgroups.
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(FwdArgs a) {
   constexpr int DL = State<D>::DL;
-  __shared__ __attribute__((aligned(16))) float Ks[kChunk][D];
-  __shared__ __attribute__((aligned(16))) float Vs[kChunk][D];
+  __shared__ __attribute__((aligned(16))) float Ks[kSplit][kChunk][D];
+  __shared__ __attribute__((aligned(16))) float Vs[kSplit][kChunk][D];
   __shared__ uint32_t selbits[kMaxBlocks / 32];
+  __shared__ float part[kSplit][kRows][kLanes][DL + 2];   // per wave: o, then m and l
 
   const int parts = a.block / kRows;            // workgroups per query block
   const int item = blockIdx.x / parts;
-  const int part = blockIdx.x - item * parts;
+  const int pr = blockIdx.x - item * parts;
   const int bh = item / a.M;
   const int I = item - bh * a.M;
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;
   const int g = h / (a.Hq / a.Hkv);
   const int t = threadIdx.x;
-  const int row = t / kLanes, sl = t % kLanes;   // query row in the block, dimension slice
-  const int qi = I * a.block + part * kRows + row;   // this lane's query token
+  const int s = __builtin_amdgcn_readfirstlane(t / kWave);   // key split of this wave
+  const int lane = t % kWave;
+  const int row = lane / kLanes, sl = lane % kLanes;   // query row, dimension slice
+  const int qi = I * a.block + pr * kRows + row;      // this lane's query token
   const bool active = qi < a.N;
   const size_t kvbase = (size_t)(b * a.Hkv + g) * a.N * D;
 
@@ -197,22 +210,25 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(FwdArgs a) {
 
   const int n_sel = a.cnt[(size_t)bh * a.M + I];
   const int32_t* list = a.idx + ((size_t)bh * a.M + I) * a.M;
-  for (int w = t; w < kMaxBlocks / 32; w += blockDim.x) selbits[w] = 0u;
-  __syncthreads();
-  for (int e = t; e < n_sel; e += blockDim.x) {
-    const int J = list[e];
-    atomicOr(&selbits[J >> 5], 1u << (J & 31));
+  if (a.approx) {
+    for (int w = t; w < kMaxBlocks / 32; w += kThreads) selbits[w] = 0u;
+    __syncthreads();
+    for (int e = t; e < n_sel; e += kThreads) {
+      const int J = list[e];
+      atomicOr(&selbits[J >> 5], 1u << (J & 31));
+    }
+    __syncthreads();
   }
 
-  // Chunk sequence: the listed blocks (ceil(block / 64) chunks each), then,
-  // with the tail on, the pooled rows of blocks [0, Jend) in chunks of 64.
-  // Chunk ci + 1 is loaded into registers while chunk ci is folded.
+  // Chunk sequence: the listed blocks (ceil(block / kChunk) chunks each),
+  // then, with the tail on, the pooled rows of blocks [0, Jend) in chunks of
+  // kChunk.  Wave s takes chunks s, s + kSplit, ...; its next chunk loads
+  // into registers while the current one is folded from its LDS chunk.
   const int per_blk = (a.block + kChunk - 1) / kChunk;
   const int n_exact = n_sel * per_blk;
   const int Jend = a.causal ? I + 1 : a.M;
   const int n_chunks = n_exact + (a.approx ? (Jend + kChunk - 1) / kChunk : 0);
   const size_t pbase = (size_t)(b * a.Hkv + g) * a.M * D;
-  // chunk ci: first row (token index, or pooled-row index for the tail) and row count
   auto chunk_rows = [&](int ci, int& first, int& n) {
     if (ci < n_exact) {
       const int k0 = list[ci / per_blk] * a.block;
@@ -228,29 +244,29 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(FwdArgs a) {
     int first, n;
     chunk_rows(ci, first, n);
     if (ci < n_exact) {
-      kr.load(a.k + kvbase + (size_t)first * D, n);
-      vr.load(a.v + kvbase + (size_t)first * D, n);
+      kr.load(a.k + kvbase + (size_t)first * D, n, lane);
+      vr.load(a.v + kvbase + (size_t)first * D, n, lane);
     } else {
-      kr.load(a.k_bar + pbase + (size_t)first * D, n);
-      vr.load(a.v_sum + pbase + (size_t)first * D, n);
+      kr.load(a.k_bar + pbase + (size_t)first * D, n, lane);
+      vr.load(a.v_sum + pbase + (size_t)first * D, n, lane);
     }
   };
-  if (n_chunks > 0) load_chunk(0);
-  for (int ci = 0; ci < n_chunks; ++ci) {
-    __syncthreads();                 // previous chunk folded by every wave
-    kr.store(Ks);
-    vr.store(Vs);
-    __syncthreads();
-    if (ci + 1 < n_chunks) load_chunk(ci + 1);
+  if (s < n_chunks) load_chunk(s);
+  for (int ci = s; ci < n_chunks; ci += kSplit) {
+    // the wave's own LDS chunk: its reads of the previous chunk precede
+    // these writes in the wave's instruction order
+    kr.store(Ks[s], lane);
+    vr.store(Vs[s], lane);
+    if (ci + kSplit < n_chunks) load_chunk(ci + kSplit);
     int first, n;
     chunk_rows(ci, first, n);
     if (ci < n_exact) {
       const int causal = a.causal;
-      fold_chunk<D>(st, Ks, Vs, n, sl, [&](int j) -> float { return (!causal || first + j <= qi) ? 1.f : 0.f; });
+      fold_chunk<D>(st, Ks[s], Vs[s], n, sl, [&](int j) -> float { return (!causal || first + j <= qi) ? 1.f : 0.f; });
     } else {
       // 0th-order tail: eligible blocks not in the list, weight n_J
       const int M = a.M, N = a.N, blk = a.block;
-      fold_chunk<D>(st, Ks, Vs, n, sl, [&](int j) -> float {
+      fold_chunk<D>(st, Ks[s], Vs[s], n, sl, [&](int j) -> float {
         const int J = first + j;
         if ((selbits[J >> 5] >> (J & 31)) & 1u) return 0.f;
         return J == M - 1 ? (float)(N - J * blk) : (float)blk;
@@ -258,19 +274,42 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(FwdArgs a) {
     }
   }
 
-  if (active) {
-    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
-    if (a.lse && sl == 0) a.lse[(size_t)bh * a.N + qi] = st.m * 0.6931471805599453f + logf(st.l);
-    float4* o = reinterpret_cast<float4*>(a.out + ((size_t)bh * a.N + qi) * D + sl * DL);
+  // merge the kSplit partial states of every row
+#pragma unroll
+  for (int c = 0; c < DL; ++c) part[s][row][sl][c] = st.o[c];
+  part[s][row][sl][DL] = st.m;
+  part[s][row][sl][DL + 1] = st.l;
+  __syncthreads();
+  if (s == 0 && active) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kSplit; ++u) m = fmaxf(m, part[u][row][sl][DL]);
+    const float ms = m == -INFINITY ? 0.f : m;
+    float l = 0.f;
+    float o[DL];
+#pragma unroll
+    for (int c = 0; c < DL; ++c) o[c] = 0.f;
+#pragma unroll
+    for (int u = 0; u < kSplit; ++u) {
+      const float w = __builtin_amdgcn_exp2f(part[u][row][sl][DL] - ms);   // 0 for an empty split
+      l = fmaf(part[u][row][sl][DL + 1], w, l);
+#pragma unroll
+      for (int c = 0; c < DL; ++c) o[c] = fmaf(part[u][row][sl][c], w, o[c]);
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (a.lse && sl == 0) a.lse[(size_t)bh * a.N + qi] = ms * 0.6931471805599453f + logf(l);
+    float4* op = reinterpret_cast<float4*>(a.out + ((size_t)bh * a.N + qi) * D + sl * DL);
 #pragma unroll
     for (int c = 0; c < DL / 4; ++c)
-      o[c] = float4{st.o[4 * c] * inv, st.o[4 * c + 1] * inv, st.o[4 * c + 2] * inv, st.o[4 * c + 3] * inv};
+      op[c] = float4{o[4 * c] * inv, o[4 * c + 1] * inv, o[4 * c + 2] * inv, o[4 * c + 3] * inv};
   }
 }
 
 template <int D>
 hipError_t run(const FwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((attn_f32_kernel<D>), dim3(a.total * (a.block / kRows)), dim3(kThreads), 0, st, a);
+  const int64_t grid = (int64_t)a.total * (a.block / kRows);
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_f32_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
