@@ -160,8 +160,12 @@ sa_status sparse_attn_select(const sa_desc* desc, const float* q_bar, const floa
  * buffers, same values, same arguments and errors as the two calls).  The
  * kernel is launched cooperatively (all its workgroups resident at once, one
  * grid-wide barrier between pooling and scoring); SA_ERR_HIP if the device
- * refuses the cooperative launch.  On MI355X the two separate calls are the
- * faster path: the barrier costs more than the launch it saves. */
+ * refuses the cooperative launch.  Kept for callers that want the routing in
+ * one launch; the library's own layer does not use it: on MI355X the two
+ * separate calls are faster (59 us against 23 + 10 us for the 8K image
+ * layer), since the grid-wide barrier, which must flush the pooled vectors
+ * out of one XCD's L2 for the other seven, costs more than the launch it
+ * saves. */
 sa_status sparse_attn_route(const sa_desc* desc, const void* q, const void* k, const void* v,
                             float* q_bar, float* k_bar, float* v_sum, void* tail, int32_t* blk_idx,
                             int32_t* blk_cnt, void* stream);
