@@ -257,7 +257,10 @@ __device__ __forceinline__ void route_item(const RouteArgs& a, int item, uint32_
     int count = 0, ties = 0;
 #pragma unroll
     for (int ch = 0; ch < MAXCH; ++ch) {
-      if (ch < nch) {
+      // threshold mode keeps a few blocks of a long row: one ballot skips a
+      // chunk with no key at or above the threshold (it has no tie to count
+      // either); top-k rows keep a share of every chunk, so they skip nothing
+      if (ch < nch && (a.mode != 0 || __ballot(key[ch] >= T_ || (diag && 64 * ch + lane == I)))) {
         const int J = 64 * ch + lane;
         const bool eq = key[ch] == T_ && J < E;
         const uint64_t beq = __ballot(eq);
