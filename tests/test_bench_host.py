@@ -67,3 +67,59 @@ def test_kernel_hash_ignores_comment_edits(tmp_path, monkeypatch):
 def test_read_traffic_needs_the_dispatched_kernel():
     assert bench.read_traffic("dit_image_8k", "attn_bf16_kernel") is None
     assert bench.read_traffic("no_such_workload", "attn_w16_kernel") is None
+
+
+class _FakeDev:
+    """Host stand-in for the device tensors the CPU-baseline parity reads
+    (indexing, .cpu(), .float(), .numpy())."""
+
+    def __init__(self, a):
+        self.a = np.asarray(a)
+
+    def __getitem__(self, key):
+        return _FakeDev(self.a[key])
+
+    def cpu(self):
+        return self
+
+    def float(self):
+        return _FakeDev(self.a.astype(np.float32))
+
+    def numpy(self):
+        return self.a
+
+
+def test_cpu_baseline_reports_stages_and_checks_parity():
+    """The CPU-baseline leg on the 1K-token workload: every stage timed, the
+    affinity core count reported, and the parity check flags a planted
+    wrong list entry and a planted wrong output (the oracle's own lists and
+    outputs pass)."""
+    import oracle
+    from synth import get_config, make_inputs
+    wl = get_config("dit_tiny_f32")
+    q, k, v = make_inputs(wl, 0)
+    ref = oracle.forward(q, k, v, block=wl.block, causal=wl.causal, approx=wl.approx, mode=wl.select,
+                         alpha=wl.alpha, density=wl.density)
+    idx, cnt = oracle.mask_to_lists(ref["mask"])
+    out = ref["out"].astype(np.float32)
+    r = bench.cpu_baseline(wl, 0, 0.0, gpu=(_FakeDev(idx), _FakeDev(cnt), _FakeDev(out)))
+    assert r["cores"] == len(os.sched_getaffinity(0)) and r["kind"] == "oracle"
+    assert set(r["stage_s"]) == {"pool_s", "score_s", "select_s", "attend_s"}
+    p = r["parity"]
+    G = wl.Hq // wl.Hkv          # a zero budget still runs one whole KV group
+    assert p["heads"] == G and p["mismatch_out_of_band"] == 0 and p["blocks_skipped"] == 0
+    assert p["blocks_compared"] == G * wl.M and p["max_abs_err"] < 1e-6
+    # plant one wrong list entry (a block the oracle did not keep) and one
+    # wrong output value in another row
+    bad_idx, bad_cnt = idx.copy(), cnt.copy()
+    row = (0, 0, 3)
+    drop = np.nonzero(~ref["mask"][row])[0][0]
+    c = int(bad_cnt[row])
+    bad_idx[row + (slice(0, c + 1),)] = np.sort(np.append(idx[row][:c], drop))
+    bad_cnt[row] += 1
+    bad_out = out.copy()
+    bad_out[0, 0, 5, 7] += 0.5
+    r = bench.cpu_baseline(wl, 0, 0.0, gpu=(_FakeDev(bad_idx), _FakeDev(bad_cnt), _FakeDev(bad_out)))
+    p = r["parity"]
+    assert p["mismatch_out_of_band"] == 1 and p["blocks_skipped"] == 1
+    assert abs(p["max_abs_err"] - 0.5) < 1e-3
