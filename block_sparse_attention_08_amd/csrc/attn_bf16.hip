@@ -638,25 +638,27 @@ __global__ __launch_bounds__(2 * BLK, 2) void attn_bf16_kernel(FwdArgs a) {
     ++e;
   }
 
-  // ---- epilogue: O / l, bf16, row q_tok; register r of d-tile nt holds
-  // d = 32*nt + 8*(r/4) + 4*hh + (r%4).
+  // ---- epilogue: O / l in bf16.  Register r of d-tile nt holds row lq,
+  // d = 32*nt + 8*(r/4) + 4*hh + (r%4); the wave's 32 rows leave through its
+  // share of the free K buffers (staged row store).
   const float lt = half_sum(st.l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   // log of the denominator: sum_a exp(z_a) = lt * 2^m
   if (a.lse && q_ok && hh == 0) a.lse[(size_t)bh * a.N + q_tok] = __logf(lt) + st.m * 0.69314718055994531f;
-  if (q_ok) {
-    uint16_t* orow = a.out + ((size_t)bh * a.N + q_tok) * D;
+  constexpr int WPB = C::NW / 2;                // waves per K buffer
+  char* stage = (w < WPB ? K0 : K1) + (w % WPB) * 32 * C::ROWB;
 #pragma unroll
-    for (int nt = 0; nt < C::NOT; ++nt) {
+  for (int nt = 0; nt < C::NOT; ++nt) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * nt + 8 * q4 + 4 * hh;
-        const u32x2 x = {pack2(st.o[nt][4 * q4] * inv, st.o[nt][4 * q4 + 1] * inv),
-                         pack2(st.o[nt][4 * q4 + 2] * inv, st.o[nt][4 * q4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d0) = x;
-      }
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int ch = 4 * nt + q4;               // 16-byte chunk of the row
+      const u32x2 x = {pack2(st.o[nt][4 * q4] * inv, st.o[nt][4 * q4 + 1] * inv),
+                       pack2(st.o[nt][4 * q4 + 2] * inv, st.o[nt][4 * q4 + 3] * inv)};
+      *reinterpret_cast<u32x2*>(stage + lq * C::ROWB + stage_slot<D>(lq, ch) * 16 + 8 * hh) = x;
     }
   }
+  const int tok0 = I * BLK + 32 * w;            // the wave's first query token
+  store_staged_rows<D, 32>(stage, a.out + ((size_t)bh * a.N + tok0) * D, a.N - tok0, lane);
 }
 
 template <int D, int BLK>

@@ -473,19 +473,22 @@ __global__ __launch_bounds__(4 * BLK, 4) void attn_w16_kernel(Args a) {
   }
   if (e < n_tiles) step(e, key0, 0, ModeC<kModeTailLast>{});
 
-  // ---- epilogue: register r of d-tile nt holds d = 16*nt + 4*lg + r
+  // ---- epilogue: O / l in bf16.  Register r of d-tile nt holds row lr,
+  // d = 16*nt + 4*lg + r; the wave's 16 rows leave through its quarter of
+  // the free K buffer (staged row store).
   const float lt = row_sum4(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   // log of the denominator: sum_a exp(z_a) = lt * 2^m
   if (a.lse && q_ok && lg == 0) a.lse[(size_t)bh * a.N + q_tok] = __logf(lt) + m * 0.69314718055994531f;
-  if (q_ok) {
-    uint16_t* orow = a.out + ((size_t)bh * a.N + q_tok) * D;
+  char* stage = Ks + w * 16 * C::ROWB;
 #pragma unroll
-    for (int nt = 0; nt < C::NOT; ++nt) {
-      const u32x2 x = {pack2(o[nt][0] * inv, o[nt][1] * inv), pack2(o[nt][2] * inv, o[nt][3] * inv)};
-      *reinterpret_cast<u32x2*>(orow + 16 * nt + 4 * lg) = x;
-    }
+  for (int nt = 0; nt < C::NOT; ++nt) {
+    const int ch = 2 * nt + (lg >> 1);          // 16-byte chunk of the row
+    const u32x2 x = {pack2(o[nt][0] * inv, o[nt][1] * inv), pack2(o[nt][2] * inv, o[nt][3] * inv)};
+    *reinterpret_cast<u32x2*>(stage + lr * C::ROWB + stage_slot<D>(lr, ch) * 16 + 8 * (lg & 1)) = x;
   }
+  const int tok0 = I * BLK + 16 * w;            // the wave's first query token
+  store_staged_rows<D, 16>(stage, a.out + ((size_t)bh * a.N + tok0) * D, a.N - tok0, lane);
 }
 
 // 64-row blocks: four 4-wave workgroups per CU (32 KB of tile buffers each).

@@ -525,6 +525,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     key = key1;
   }
 
+  // dq straight from the fragments: a staged store would take this pass
+  // (128 registers at four waves per SIMD) past its register budget
   if (q_ok) {
     uint16_t* orow = a.dq + qrow * D;
 #pragma unroll
@@ -734,10 +736,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
     }
     __syncthreads();
   }
-  if (k_ok) {
+  // dk, dv of the wave's 16 keys (row lr, d = 16*nt + 4*lg + r) through its
+  // quarters of the free Q1 and O1 buffers (staged row store; Q0 holds the
+  // pooled sums)
+  {
     const float n = (float)min(BLK, a.N - J * BLK);
-    uint16_t* kr = a.dk + krow * D;
-    uint16_t* vr = a.dv + krow * D;
+    char* sk = Q1 + w * 16 * C::ROWB;
+    char* sv = O1 + w * 16 * C::ROWB;
 #pragma unroll
     for (int nt = 0; nt < C::NOT; ++nt) {
       const int d0 = 16 * nt + 4 * lg;
@@ -746,9 +751,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdArgs a) {
         x += *reinterpret_cast<const f32x4*>(pooled + d0) / n;
         y += *reinterpret_cast<const f32x4*>(pooled + D + d0) / n;
       }
-      *reinterpret_cast<u32x2*>(kr + d0) = u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])};
-      *reinterpret_cast<u32x2*>(vr + d0) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
+      const int off = lr * C::ROWB + stage_slot<D>(lr, 2 * nt + (lg >> 1)) * 16 + 8 * (lg & 1);
+      *reinterpret_cast<u32x2*>(sk + off) = u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])};
+      *reinterpret_cast<u32x2*>(sv + off) = u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])};
     }
+    const int tok0 = J * BLK + 64 * part + 16 * w;   // the wave's first key token
+    const size_t obase = ((size_t)grp * a.N + tok0) * D;
+    store_staged_rows<D, 16>(sk, a.dk + obase, a.N - tok0, lane);
+    store_staged_rows<D, 16>(sv, a.dv + obase, a.N - tok0, lane);
   }
 }
 

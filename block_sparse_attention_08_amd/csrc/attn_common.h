@@ -52,4 +52,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
 }
 
+// Output rows staged in LDS.  A wave's output rows are consecutive in
+// memory, but its accumulator fragments hold 8-byte pieces of many rows; a
+// store straight from them touches a cache line per row in every
+// instruction.  Instead the wave writes its fragments into a free LDS area
+// (row r at r * 2D bytes, its 16-byte chunk c in slot stage_slot(r, c), a
+// swizzle that spreads a column of rows over the banks) and then stores
+// whole 16-byte chunks, 64 / (D/8) consecutive rows per instruction.
+template <int D>
+__device__ __forceinline__ int stage_slot(int r, int c) { return c ^ (r & (D / 8 - 1)); }
+
+// The store half: ROWS staged rows to out[0 .. nrows) (rows at or past
+// nrows are not written), non-temporal (the output is not read again by the
+// kernel).  The wave's own LDS writes must precede it; the fences order them
+// for the other lanes of the wave.
+template <int D, int ROWS>
+__device__ __forceinline__ void store_staged_rows(const char* stage, uint16_t* out, int nrows, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int RPI = 64 / CPR;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int i = 0; i < ROWS / RPI; ++i) {
+    const int r = RPI * i + lane / CPR;
+    const int c = lane % CPR;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * (2 * D) + stage_slot<D>(r, c) * 16);
+    if (r < nrows) __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(out + (size_t)r * D + c * 8));
+  }
+}
+
 }  // namespace sa
