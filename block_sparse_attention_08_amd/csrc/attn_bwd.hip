@@ -538,6 +538,244 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// dq for 128-row blocks: two 16-row groups per wave, so every K, V and K^T
+// fragment read from LDS feeds the products of both groups (half the LDS
+// operand bytes per product of the one-group form above; −13% on the dq
+// pass at 128K).  Workgroup = one query block, four waves of 32 rows, two
+// workgroups per CU (234 registers).  Same arithmetic, in the same order, as
+// the one-group form: the gradients are bit-identical.
+template <int D>
+__device__ __forceinline__ void gemm_rows_g2(f32x4 (&acc)[2][4], const char* tile, const Frag<D>& f,
+                                             const bf16x8 (&rg)[2][BC<D>::NKS]) {
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) acc[g][tg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < BC<D>::NKS; ++s)
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(tile + f.rb[s] + 16 * tg * BC<D>::ROWB);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) acc[g][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rg[g][s], acc[g][tg], 0, 0, 0);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void gemm_tr_g2(f32x4 (&acc)[2][BC<D>::NOT], const char* tile, const Frag<D>& f,
+                                           const bf16x8 (&pk)[2][2]) {
+#pragma unroll
+  for (int nt = 0; nt < BC<D>::NOT; ++nt)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const bf16x8 a = tr_frag<D>(tile, f, nt, cc);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) acc[g][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk[g][cc], acc[g][nt], 0, 0, 0);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq2_kernel(BwdArgs a) {
+  constexpr int BLK = 128;
+  constexpr int NW = 4;
+  constexpr int NT = 64 * NW;
+  constexpr int SUB = BLK / BT;                // 64-key tiles per block
+  using C = BC<D>;
+  using DM = Dma<D, NW>;
+  __shared__ __attribute__((aligned(1024))) char Kt[C::TB];
+  __shared__ __attribute__((aligned(1024))) char Vt[C::TB];
+  __shared__ uint32_t selbits[kMaxBlocks / 32];
+  __shared__ uint16_t tail_rows[kMaxBlocks];
+
+  const int total = a.B * a.Hq * a.M;
+  const int item = xcd_local_item(blockIdx.x, total);
+  if (item < 0) return;
+  const int hg = item % a.G;
+  int rest = item / a.G;
+  const int I = a.M - 1 - rest % a.M;
+  rest /= a.M;
+  const int g = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  const int h = g * a.G + hg;
+  const int bh = b * a.Hq + h;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  // row group rg: query row I*BLK + 32w + 16rg + lr
+  int q_tok[2];
+  bf16x8 qf[2][C::NKS], gf[2][C::NKS];
+  float nLc[2], Dd[2];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    q_tok[rg] = I * BLK + 32 * w + 16 * rg + lr;
+    const bool ok = q_tok[rg] < a.N;
+    const size_t qrow = (size_t)bh * a.N + (ok ? q_tok[rg] : 0);
+    load_row<D>(qf[rg], a.q + qrow * D, ok, lg);
+    load_row<D>(gf[rg], a.dout + qrow * D, ok, lg);
+    nLc[rg] = ok ? a.delta[(size_t)a.B * a.Hq * a.N + qrow] : -INFINITY;   // P = 0 on padding rows
+    Dd[rg] = ok ? a.delta[qrow] : 0.f;
+  }
+
+  const int n_sel = scalar_view(a.cnt)[(size_t)bh * a.M + I];
+  const const_i32* list = scalar_view(a.idx + ((size_t)bh * a.M + I) * a.M);
+  const int Jend = a.causal ? I + 1 : a.M;
+  const int last_n = a.N - (a.M - 1) * BLK;
+  const int n_rest = a.approx ? Jend - n_sel : 0;
+  const int n_tt = (n_rest + BT - 1) / BT;
+  int edge = 0;
+  if (n_sel > 0) {
+    const int J = list[n_sel - 1];
+    edge = ((J + 1) * BLK > a.N || (a.causal && J >= I)) ? 1 : 0;
+  }
+  const int n_exact = SUB * n_sel;
+  const int n_plain = n_exact - SUB * edge;
+  const int n_tiles = n_exact + n_tt;
+  const float log2_blk = __log2f((float)BLK);
+  const float last_fix = (__log2f((float)last_n) - log2_blk) / a.scale_log2;
+
+  if (a.approx) {
+    for (int i = t; i < kMaxBlocks / 32; i += NT) selbits[i] = 0u;
+    __syncthreads();
+    for (int e = t; e < n_sel; e += NT) {
+      const int J = list[e];
+      atomicOr(&selbits[J >> 5], 1u << (J & 31));
+    }
+    __syncthreads();
+    if (w == 0) {
+      int base = 0;
+      for (int J0 = 0; J0 < Jend; J0 += 64) {
+        const int J = J0 + lane;
+        const int Jc = J < Jend ? J : 0;
+        const bool rest_J = J < Jend && !((selbits[Jc >> 5] >> (Jc & 31)) & 1u);
+        const uint64_t bal = __ballot(rest_J);
+        if (rest_J) tail_rows[base + lanes_below(bal)] = (uint16_t)J;
+        base += __popcll(bal);
+      }
+    }
+    __syncthreads();
+  }
+
+  const int head_bytes = a.N * C::ROWB;
+  const size_t kv_off = (size_t)(b * a.Hkv + g) * a.N * D;
+  const size_t pp_off = (size_t)(b * a.Hkv + g) * a.M * D;
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(a.k + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(a.v + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t tkrs = head_rsrc(a.approx ? a.tail_k + pp_off : a.k, a.M * C::ROWB);
+  const __amdgpu_buffer_rsrc_t tvrs = head_rsrc(a.approx ? a.tail_v + pp_off : a.v, a.M * C::ROWB);
+  const int row0 = DM::row0(w, lane);
+  const int col = DM::col(w, lane);
+  const int voff = row0 * C::ROWB + col;
+  const Frag<D> fr(lr, lg);
+
+  auto tile_key = [&](int e) -> int {
+    return e < n_exact ? list[e / SUB] * BLK + (e % SUB) * BT : e - n_exact;
+  };
+  auto issue = [&](int e, int key, bool is_v) {
+    char* dst = is_v ? Vt : Kt;
+    if (e < n_exact) {
+      DM::tile(is_v ? vrs : krs, key * C::ROWB, dst, w, voff);
+    } else {
+      int ro[DM::NI];
+#pragma unroll
+      for (int i = 0; i < DM::NI; ++i) {
+        const int r = BT * key + row0 + i * NW * C::RPK;
+        ro[i] = (r < n_rest ? (int)tail_rows[r] : 0) * C::ROWB;
+      }
+      DM::rows(is_v ? tvrs : tkrs, ro, col, dst, w);
+    }
+  };
+
+  f32x4 dq[2][C::NOT];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+    for (int i = 0; i < C::NOT; ++i) dq[rg][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float c = a.scale_log2;
+
+  int key = n_tiles > 0 ? tile_key(0) : 0;
+  if (n_tiles > 0) {
+    issue(0, key, false);
+    issue(0, key, true);
+  }
+  wait_vm();
+  __syncthreads();
+  for (int e = 0; e < n_tiles; ++e) {
+    f32x4 s[2][4], dp[2][4];
+    __builtin_amdgcn_s_setprio(1);
+    gemm_rows_g2<D>(s, Kt, fr, qf);
+    gemm_rows_g2<D>(dp, Vt, fr, gf);
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();                           // V tile free
+    const int key1 = e + 1 < n_tiles ? tile_key(e + 1) : 0;
+    if (e + 1 < n_tiles) issue(e + 1, key1, true);
+
+    float lb = 0.f;
+    if (e >= n_exact) {
+      lb = log2_blk;
+      if (e == n_tiles - 1) {
+        const int lim = n_rest - BT * key - 4 * lg;
+        const int fix_kr = (last_n != BLK && tail_rows[n_rest - 1] == a.M - 1) ? lim - 1 : -1;
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+          for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int kr = 16 * tg + r;
+              s[rg][tg][r] = kr < lim ? (kr == fix_kr ? s[rg][tg][r] + last_fix : s[rg][tg][r]) : -INFINITY;
+            }
+      }
+    } else if (e >= n_plain) {
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+        int lim = a.N - key;
+        if (a.causal) lim = min(lim, q_tok[rg] - key + 1);
+        lim -= 4 * lg;
+#pragma unroll
+        for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[rg][tg][r] = 16 * tg + r < lim ? s[rg][tg][r] : -INFINITY;
+      }
+    }
+    bf16x8 pk[2][2];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      const float off = lb + nLc[rg];
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[rg][tg][r], c, off));
+          s[rg][tg][r] = p * (dp[rg][tg][r] - Dd[rg]);
+        }
+      pack_rows(s[rg], pk[rg]);
+    }
+    __builtin_amdgcn_s_setprio(1);
+    gemm_tr_g2<D>(dq, Kt, fr, pk);             // dQ^T += K^T dS^T
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();                           // K tile free
+    if (e + 1 < n_tiles) issue(e + 1, key1, false);
+    wait_vm();
+    __syncthreads();
+    key = key1;
+  }
+
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    if (q_tok[rg] < a.N) {
+      uint16_t* orow = a.dq + ((size_t)bh * a.N + q_tok[rg]) * D;
+#pragma unroll
+      for (int nt = 0; nt < C::NOT; ++nt) {
+        const u32x2 x = {pack2(dq[rg][nt][0] * a.scale, dq[rg][nt][1] * a.scale),
+                         pack2(dq[rg][nt][2] * a.scale, dq[rg][nt][3] * a.scale)};
+        *reinterpret_cast<u32x2*>(orow + 16 * nt + 4 * lg) = x;
+      }
+    }
+  }
+}
+
 // --------------------------------------------------- dk/dv and pooled grads
 // Shared body: NW waves, 16 register rows each (keys or pooled rows); loops
 // over 64-row query tiles handed out by `next`.  POOLED: register rows are
@@ -912,8 +1150,13 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, st, a);
   hipLaunchKernelGGL(bwd_bitmap_kernel, dim3(a.B * a.Hq * a.M), dim3(64), 0, st, a);
   hipLaunchKernelGGL(bwd_cols_kernel, dim3(a.B * a.Hkv * a.W), dim3(64), 0, st, a);
-  const int nq = a.B * a.Hq * a.M * (BLK / 64);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, BLK>), dim3(8 * ((nq + 7) / 8)), dim3(256), 0, st, a);
+  if constexpr (BLK == 128) {
+    const int nq = a.B * a.Hq * a.M;
+    hipLaunchKernelGGL((bwd_dq2_kernel<D>), dim3(8 * ((nq + 7) / 8)), dim3(256), 0, st, a);
+  } else {
+    const int nq = a.B * a.Hq * a.M * (BLK / 64);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, BLK>), dim3(8 * ((nq + 7) / 8)), dim3(256), 0, st, a);
+  }
   if (a.approx) {
     const int tiles = (a.M + BT - 1) / BT;
     hipLaunchKernelGGL((bwd_dtail_kernel<D, BLK>), dim3(a.B * a.Hkv * tiles * kTailChunks), dim3(256), 0, st,
