@@ -29,6 +29,7 @@ CASES = [
     (1, 2, 2, 2600, 128, 128, True, True, "alpha"),      # 128-row blocks, causal + tail
     (2, 2, 2, 640, 128, 64, False, False, "density"),
     (1, 2, 2, 300, 64, 128, False, True, "density"),     # d = 64, 128-row blocks, tail
+    (2, 4, 2, 700, 128, 128, True, True, "alpha"),       # batch 2, GQA, 128-row blocks (two-group dq pass)
 ]
 
 
