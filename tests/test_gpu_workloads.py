@@ -156,22 +156,28 @@ def test_dense_lists_at_256k():
     assert worst <= TOL_OUT["bf16"]
 
 
-def test_topk_and_tail_at_2048_blocks():
+@pytest.mark.parametrize("causal,mode,Hq,Hkv", [(False, "density", 2, 2), (True, "alpha", 4, 2)],
+                         ids=["topk_full", "alpha_causal_gqa"])
+def test_tail_at_2048_blocks(causal, mode, Hq, Hkv):
     """The largest row the library takes with 64-row blocks: N = 131072, M =
-    2048 (`kMaxBlocks`), top-k at density 0.05 (k = 103, the 32-pass radix
-    select over 2048 keys per row) with the 0th-order tail (1945 pooled rows
-    per query block, 61 tail tiles), non-causal, two heads, the clustered
-    generator.  Lists on every row bit-exact outside the band; outputs of 16
-    sampled query blocks against the oracle on its own selection; every
-    output element written."""
+    2048 (`kMaxBlocks`), with the 0th-order tail, the clustered generator.
+    Non-causal top-k at density 0.05 (k = 103, the 32-pass radix select over
+    2048 keys per row; 1945 pooled rows, 61 tail tiles per query block), and
+    causal alpha = 0.5 with grouped queries (the diagonal forced exact, the
+    tail over the earlier blocks).  Lists on every row bit-exact outside the
+    band; outputs of 16 sampled query blocks against the oracle on its own
+    selection; every output element written."""
     import torch
     import block_sparse_attention_08_amd as bsa
     from synth import random_qkv
-    B, H, N, d, block, density = 1, 2, 131072, 128, 64, 0.05
+    B, N, d, block, density, alpha = 1, 131072, 128, 64, 0.05, 0.5
+    H = Hq
     M = N // block
-    say("2048 blocks of 64 rows, top-k 5% + tail: generating inputs")
-    q, k, v = random_qkv(B, H, H, N, d, seed=31, block=block, dtype="bf16", kind="cluster", noise=0.5)
-    desc = bsa.make_desc(B, H, H, N, d, block=block, dtype="bf16", density=density, causal=False, approx=True)
+    say(f"2048 blocks of 64 rows, {mode}, causal={causal}, tail: generating inputs")
+    q, k, v = random_qkv(B, Hq, Hkv, N, d, seed=31, block=block, dtype="bf16", kind="cluster", noise=0.5)
+    desc = bsa.make_desc(B, Hq, Hkv, N, d, block=block, dtype="bf16",
+                         density=density if mode == "density" else None,
+                         alpha=alpha if mode == "alpha" else None, causal=causal, approx=True)
     qd, kd, vd = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in (q, k, v))
     ws = bsa.Workspace(desc)
     out = torch.full_like(qd, float("nan"))
@@ -181,17 +187,18 @@ def test_topk_and_tail_at_2048_blocks():
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all()), "output has unwritten or non-finite elements"
     cnt, idx = to_host(ws.blk_cnt), to_host(ws.blk_idx)
-    kk = int(np.ceil(density * M - 1e-9))
-    assert np.all(cnt == kk), (int(cnt.min()), int(cnt.max()), kk)
+    if mode == "density":
+        kk = int(np.ceil(density * M - 1e-9))
+        assert np.all(cnt == kk), (int(cnt.min()), int(cnt.max()), kk)
     mask = np.zeros((B, H, M, M), dtype=bool)
     for pos in np.ndindex(*cnt.shape):
-        mask[pos + (idx[pos][:kk],)] = True
+        mask[pos + (idx[pos][:int(cnt[pos])],)] = True
     rng = np.random.default_rng(7)
     rows = sorted({(0, int(rng.integers(H)), int(rng.integers(M))) for _ in range(14)} | {(0, 0, 0), (0, H - 1, M - 1)})
     say(f"  oracle: selection on every row, attention on {len(rows)} query blocks")
-    ref = oracle.forward(q, k, v, block=block, causal=False, approx=True, mode="density", density=density,
-                         rows=rows)
-    band = oracle.band_mask(ref["scores"], ref["thresholds"], False)
+    ref = oracle.forward(q, k, v, block=block, causal=causal, approx=True, mode=mode, density=density,
+                         alpha=alpha, rows=rows)
+    band = oracle.band_mask(ref["scores"], ref["thresholds"], causal)
     diff = mask != ref["mask"]
     assert not (diff & ~band).any(), f"{int((diff & ~band).sum())} mask mismatches outside the band"
     row_diff = diff.any(-1)
