@@ -163,10 +163,12 @@ def read_traffic(workload, kernel):
 
 def achievable_peaks(dev, read_mib=2048, reps=5, mfma_iters=20000, lds_iters=20000):
     """Rates the machine reaches with the measurement kernels of
-    libsa_peaks.so: a streaming read of a buffer 8x the last-level cache, a
-    loop of independent bf16 matrix-core products and a loop of 16-byte LDS
-    reads, timed with events on the launch stream.  Returns HBM GB/s, MFMA
-    TFLOP/s and LDS GB/s per compute unit."""
+    libsa_peaks.so: a streaming read of a buffer 8x the last-level cache,
+    loops of independent bf16 matrix-core products (on one operand pair, and
+    on changing data: the chip holds a lower clock for the latter) and a loop
+    of 16-byte LDS reads, timed with events on the launch stream.  Returns
+    HBM GB/s, MFMA TFLOP/s (one pair), MFMA TFLOP/s (changing data) and LDS
+    GB/s per compute unit."""
     import ctypes
     import torch
     from block_sparse_attention_08_amd import _lib
@@ -192,11 +194,15 @@ def achievable_peaks(dev, read_mib=2048, reps=5, mfma_iters=20000, lds_iters=200
                                           st.cuda_stream, ctypes.byref(got)))
     t_mfma = timed(lambda: h.sa_peak_mfma_bf16(mfma_iters, sink.data_ptr(), st.cuda_stream,
                                                ctypes.byref(flops)))
+    dflops = ctypes.c_double(0.0)
+    t_data = timed(lambda: h.sa_peak_mfma_bf16_data(max(1, mfma_iters // 2), sink.data_ptr(), st.cuda_stream,
+                                                    ctypes.byref(dflops)))
     lds = ctypes.c_double(0.0)
     t_lds = timed(lambda: h.sa_peak_lds_read(lds_iters, sink.data_ptr(), st.cuda_stream, ctypes.byref(lds)))
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     del buf
-    return got.value / t_read / 1e9, flops.value / t_mfma / 1e12, lds.value / t_lds / 1e9 / cus
+    return (got.value / t_read / 1e9, flops.value / t_mfma / 1e12, dflops.value / t_data / 1e12,
+            lds.value / t_lds / 1e9 / cus)
 
 
 def _cpu_model():
@@ -563,7 +569,7 @@ def main():
             "note": "step = pool + select + fwd_lse + bwd; value/ms_per_step include the backward"}
     if not args.no_peaks:
         print("[bench] measuring achievable HBM read, bf16 MFMA and LDS read rates", file=sys.stderr, flush=True)
-        hbm, mfma, lds = achievable_peaks(dev)
+        hbm, mfma, mfma_data, lds = achievable_peaks(dev)
         pool_gbps = pool_bytes / (ms_pool * 1e-3) / 1e9
         lds_bytes = (lds_operand_bytes(cnt_h, wl.block, wl.d, wl.causal, wl.approx and not args.dense,
                                        attn_kernel) if wl.dtype == "bf16" else None)
@@ -579,6 +585,9 @@ def main():
                 (pool_bytes + sel_bytes) / ((ms_pool + ms_sel) * 1e-3) / 1e9 / hbm, 4),
             "fwd_frac_of_achievable_mfma": (round(eff_tflops_fwd / mfma, 4)
                                             if wl.dtype == "bf16" else None),
+            "mfma_bf16_data_TFLOPs": round(mfma_data, 1),
+            "fwd_frac_of_data_mfma": (round(eff_tflops_fwd / mfma_data, 4)
+                                      if wl.dtype == "bf16" else None),
         }
     if not (args.dense or args.no_dense_compare or args.backward):
         print("[bench] dense comparison: every eligible block listed", file=sys.stderr, flush=True)

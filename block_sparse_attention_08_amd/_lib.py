@@ -121,6 +121,8 @@ def peaks_lib() -> ctypes.CDLL:
             h.sa_peak_read.restype = ctypes.c_int
             h.sa_peak_mfma_bf16.argtypes = [ctypes.c_int, _P, _P, ctypes.POINTER(ctypes.c_double)]
             h.sa_peak_mfma_bf16.restype = ctypes.c_int
+            h.sa_peak_mfma_bf16_data.argtypes = [ctypes.c_int, _P, _P, ctypes.POINTER(ctypes.c_double)]
+            h.sa_peak_mfma_bf16_data.restype = ctypes.c_int
             h.sa_peak_lds_read.argtypes = [ctypes.c_int, _P, _P, ctypes.POINTER(ctypes.c_double)]
             h.sa_peak_lds_read.restype = ctypes.c_int
             _peaks = h

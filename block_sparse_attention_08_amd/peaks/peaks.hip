@@ -1,7 +1,8 @@
 // Achievable-rate kernels for the roofline denominators, measured on the
 // machine at hand next to the datasheet peaks: a streaming read over a buffer
-// much larger than the last-level cache (HBM), a loop of independent bf16
-// matrix-core products (MFMA), and a loop of 16-byte LDS reads (the operand
+// much larger than the last-level cache (HBM), loops of independent bf16
+// matrix-core products (MFMA) on one operand pair and on changing data, and
+// a loop of 16-byte LDS reads (the operand
 // path of the attention kernels).  Measurement only; nothing on the attention
 // path calls them.
 #include <hip/hip_runtime.h>
@@ -67,6 +68,48 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(int iters, float seed, u
   if (s == 1234.5f) sink[blockIdx.x & 255] = __float_as_uint(s);
 }
 
+// The same products over changing data: eight operand pairs of random bits
+// (bf16 values in [-2, 2)) taken in turn, B rotated against A per chain.  A
+// loop on one operand pair toggles few bits in the matrix cores and draws
+// less power than products over real data, and the clock the chip holds
+// under load follows the power it draws; this loop gives the rate for data
+// that changes with every product.  Two 256-thread workgroups per CU (the
+// operand registers leave room for two waves per SIMD; four independent
+// chains per wave keep the matrix core fed).
+constexpr int kPairs = 8;
+
+__global__ __launch_bounds__(kThreads) void mfma_data_kernel(int iters, uint32_t seed, uint32_t* sink) {
+  bf16x8 a[kPairs], b[kPairs];
+  uint32_t x = seed ^ (threadIdx.x * 2654435761u) ^ (blockIdx.x * 40503u);
+#pragma unroll
+  for (int u = 0; u < kPairs; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x ^= x << 13; x ^= x >> 17; x ^= x << 5;       // xorshift32
+      a[u][e] = (__bf16)((float)(x & 0xFFFFu) * (1.0f / 16384.0f) - 2.0f);
+      x ^= x << 13; x ^= x >> 17; x ^= x << 5;
+      b[u][e] = (__bf16)((float)(x & 0xFFFFu) * (1.0f / 16384.0f) - 2.0f);
+    }
+  f32x16 c[kChains];
+#pragma unroll
+  for (int i = 0; i < kChains; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[i][r] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < kPairs; ++u)
+#pragma unroll
+      for (int i = 0; i < kChains; ++i)
+        c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[(u + i) % kPairs], c[i], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kChains; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c[i][r];
+  if (s == 1234.5f) sink[blockIdx.x & 255] = __float_as_uint(s);
+}
+
 // LDS read rate: four 256-thread workgroups per CU, each filling 32 KB of
 // LDS once, then per trip 16 ds_read_b128 per wave (1 KB each, contiguous
 // per instruction, so free of bank conflicts) kept in flight together; an
@@ -123,6 +166,16 @@ SA_PEAKS_EXPORT int sa_peak_mfma_bf16(int iters, void* sink, void* stream, doubl
   if (grid <= 0) return (int)hipErrorInvalidDevice;
   *flops = (double)grid * (kThreads / 64) * (double)iters * kChains * kFlopsPerMfma;
   hipLaunchKernelGGL(mfma_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, iters, 1.0e-3f,
+                     (uint32_t*)sink);
+  return (int)hipGetLastError();
+}
+
+SA_PEAKS_EXPORT int sa_peak_mfma_bf16_data(int iters, void* sink, void* stream, double* flops) {
+  if (!sink || !flops || iters < 1) return (int)hipErrorInvalidValue;
+  const int grid = grid_for(2);
+  if (grid <= 0) return (int)hipErrorInvalidDevice;
+  *flops = (double)grid * (kThreads / 64) * (double)iters * kPairs * kChains * kFlopsPerMfma;
+  hipLaunchKernelGGL(mfma_data_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, iters, 12345u,
                      (uint32_t*)sink);
   return (int)hipGetLastError();
 }

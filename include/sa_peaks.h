@@ -39,6 +39,14 @@ SA_PEAKS_EXPORT int sa_peak_read(const void* buf, size_t bytes, void* sink, void
  * as above. */
 SA_PEAKS_EXPORT int sa_peak_mfma_bf16(int iters, void* sink, void* stream, double* flops);
 
+/* Run `iters` rounds of 32 products per wave (eight operand pairs of random
+ * bf16 values in [-2, 2), taken in turn, on four independent 32x32x16
+ * accumulator chains) on two 256-thread workgroups per compute unit;
+ * *flops as above.  Products over changing data draw more power than the
+ * one-pair loop above, and the chip's clock under load follows its power:
+ * this is the product rate for data like an attention kernel's. */
+SA_PEAKS_EXPORT int sa_peak_mfma_bf16_data(int iters, void* sink, void* stream, double* flops);
+
 /* Run `iters` rounds of sixteen 16-byte LDS reads per lane (ds_read_b128,
  * bank-conflict free, all in flight together) on four 256-thread workgroups
  * per compute unit, each reading its own 32 KB of LDS; *bytes receives the
