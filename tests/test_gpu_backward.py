@@ -30,6 +30,7 @@ CASES = [
     (2, 2, 2, 640, 128, 64, False, False, "density"),
     (1, 2, 2, 300, 64, 128, False, True, "density"),     # d = 64, 128-row blocks, tail
     (2, 4, 2, 700, 128, 128, True, True, "alpha"),       # batch 2, GQA, 128-row blocks (two-group dq pass)
+    (1, 4, 2, 1400, 64, 128, True, True, "alpha"),       # d = 64 two-group dq pass, causal + tail, GQA, 10*128 + 120
 ]
 
 

@@ -31,6 +31,8 @@ CASES = [
     (1, 2, 2, 640, 64, 64, "f32", False, True, "alpha"),
     (1, 2, 1, 555, 128, 128, "f32", True, False, "density"),
     (1, 3, 3, 777, 128, 64, "f32", True, True, "density"),
+    (1, 2, 1, 1500, 64, 128, "bf16", True, True, "alpha"),      # d = 64, 128-row blocks, causal + tail, GQA, 11*128 + 92
+    (1, 2, 2, 700, 64, 128, "f32", False, True, "alpha"),       # f32, 128-row blocks, tail, 5*128 + 60
 ]
 
 
