@@ -226,7 +226,10 @@ def cpu_baseline(wl, seed, budget_s, gpu=None):
     the first pass over each group is also a parity check of that run: the
     GPU's lists against the oracle's (bit-exact outside the 1e-5 band around
     the threshold; band blocks counted) and the GPU's outputs against the
-    oracle's on every query block whose selection agrees (max-abs)."""
+    oracle's on every query block whose selection agrees (max-abs).  The
+    lists of the groups the timed passes did not reach are then checked too
+    (pooling, scores and selection only, untimed: cheap next to attention),
+    so the selection is compared on every head."""
     import oracle
     from synth import make_group
     try:
@@ -238,6 +241,17 @@ def cpu_baseline(wl, seed, budget_s, gpu=None):
     M = wl.M
     scale = 1.0 / np.sqrt(wl.d)
     bounds = oracle.block_bounds(wl.N, wl.block)
+
+    def list_diff(gidx, gcnt, heads, sel, sc, thr):
+        """(GPU mask != oracle mask, oracle band) over the query heads `heads`."""
+        gc = gcnt[0, heads].cpu().numpy()
+        gi = gidx[0, heads].cpu().numpy()
+        gmask = np.zeros((1, len(heads), M, M), bool)
+        for hl in range(len(heads)):
+            for I in range(M):
+                gmask[0, hl, I, gi[hl, I, :gc[hl, I]]] = True
+        return gmask != sel, oracle.band_mask(sc, thr, wl.causal)
+
     elig = oracle.eligible_mask(M, wl.causal)
     t_stage = {"pool_s": 0.0, "score_s": 0.0, "select_s": 0.0, "attend_s": 0.0}
     flops = 0.0
@@ -279,14 +293,7 @@ def cpu_baseline(wl, seed, budget_s, gpu=None):
             checked.add(g)
             gidx, gcnt, gout = gpu
             heads = list(range(g * G, (g + 1) * G))
-            gc = gcnt[0, heads].cpu().numpy()
-            gi = gidx[0, heads].cpu().numpy()
-            gmask = np.zeros((1, G, M, M), bool)
-            for hl in range(G):
-                for I in range(M):
-                    gmask[0, hl, I, gi[hl, I, :gc[hl, I]]] = True
-            band = oracle.band_mask(sc, thr, wl.causal)
-            diff = gmask != sel
+            diff, band = list_diff(gidx, gcnt, heads, sel, sc, thr)
             par["heads"] += G
             par["band_blocks"] += int(band.sum())
             par["band_differ"] += int((diff & band).sum())
@@ -304,6 +311,27 @@ def cpu_baseline(wl, seed, budget_s, gpu=None):
                     par["blocks_compared"] += 1
         groups += 1
     spent = sum(t_stage.values())
+    if gpu is not None:
+        # the selection of every head: the groups the timed passes reached,
+        # then the rest (pooling, scores and selection only, not timed)
+        allm = {"heads": par["heads"], "band_blocks": par["band_blocks"], "band_differ": par["band_differ"],
+                "mismatch_out_of_band": par["mismatch_out_of_band"]}
+        for g in range(wl.Hkv):
+            if g in checked:
+                continue
+            q, k, _ = make_group(wl, seed, 0, g)
+            q_bar = oracle.pool_mean(q[None], wl.block)
+            k_bar = oracle.pool_mean(k[None, None], wl.block)
+            sc = oracle.block_scores(q_bar, k_bar, scale)
+            sel = oracle.select(sc, causal=wl.causal, approx=wl.approx, mode=wl.select, alpha=wl.alpha,
+                                density=wl.density)
+            thr = oracle.thresholds(sc, causal=wl.causal, mode=wl.select, alpha=wl.alpha, density=wl.density)
+            diff, band = list_diff(gpu[0], gpu[1], list(range(g * G, (g + 1) * G)), sel, sc, thr)
+            allm["heads"] += G
+            allm["band_blocks"] += int(band.sum())
+            allm["band_differ"] += int((diff & band).sum())
+            allm["mismatch_out_of_band"] += int((diff & ~band).sum())
+        par["lists_all_heads"] = allm
     if groups >= wl.Hkv:
         what = (f"all {wl.Hq} query heads, {groups / wl.Hkv:.2f} passes over the workload"
                 if groups % wl.Hkv else f"all {wl.Hq} query heads x {groups // wl.Hkv} passes")

@@ -109,6 +109,8 @@ def test_cpu_baseline_reports_stages_and_checks_parity():
     G = wl.Hq // wl.Hkv          # a zero budget still runs one whole KV group
     assert p["heads"] == G and p["mismatch_out_of_band"] == 0 and p["blocks_skipped"] == 0
     assert p["blocks_compared"] == G * wl.M and p["max_abs_err"] < 1e-6
+    # the lists of every head are compared, not only the timed group's
+    assert p["lists_all_heads"]["heads"] == wl.Hq and p["lists_all_heads"]["mismatch_out_of_band"] == 0
     # plant one wrong list entry (a block the oracle did not keep) and one
     # wrong output value in another row
     bad_idx, bad_cnt = idx.copy(), cnt.copy()
@@ -123,3 +125,16 @@ def test_cpu_baseline_reports_stages_and_checks_parity():
     p = r["parity"]
     assert p["mismatch_out_of_band"] == 1 and p["blocks_skipped"] == 1
     assert abs(p["max_abs_err"] - 0.5) < 1e-3
+    assert p["lists_all_heads"]["mismatch_out_of_band"] == 1
+    # a wrong entry in a head outside the timed group shows only in the
+    # all-heads list check
+    assert wl.Hq > G
+    bad_idx, bad_cnt = idx.copy(), cnt.copy()
+    row = (0, wl.Hq - 1, 2)
+    drop = np.nonzero(~ref["mask"][row])[0][0]
+    c = int(bad_cnt[row])
+    bad_idx[row + (slice(0, c + 1),)] = np.sort(np.append(idx[row][:c], drop))
+    bad_cnt[row] += 1
+    r = bench.cpu_baseline(wl, 0, 0.0, gpu=(_FakeDev(bad_idx), _FakeDev(bad_cnt), _FakeDev(out)))
+    p = r["parity"]
+    assert p["mismatch_out_of_band"] == 0 and p["lists_all_heads"]["mismatch_out_of_band"] == 1
