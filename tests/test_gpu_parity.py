@@ -33,6 +33,7 @@ CASES = [
     (1, 3, 3, 777, 128, 64, "f32", True, True, "density"),
     (1, 2, 1, 1500, 64, 128, "bf16", True, True, "alpha"),      # d = 64, 128-row blocks, causal + tail, GQA, 11*128 + 92
     (1, 2, 2, 700, 64, 128, "f32", False, True, "alpha"),       # f32, 128-row blocks, tail, 5*128 + 60
+    (1, 2, 1, 4100, 128, 64, "f32", True, True, "alpha"),       # f32, 65 blocks (64*64 + 4), causal + tail, GQA
 ]
 
 
