@@ -66,7 +66,10 @@
  *
  * Ownership and threading: the caller allocates and frees every buffer
  * (sizes from sparse_attn_buffer_sizes).  The library never allocates, frees
- * or synchronises, keeps no state between calls and is reentrant.  Each
+ * or synchronises and keeps no state between calls, except for the one
+ * fixed device array that sparse_attn_bwd_noalloc uses as its scratch (see
+ * there: calls of that entry point that overlap on one device race); every
+ * other entry point is reentrant.  Each
  * compute call validates its arguments on the host, then enqueues kernels on
  * the caller's HIP stream (`stream`, a hipStream_t; NULL = default stream)
  * and returns without waiting.
